@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the Jamba Mamba-1 mixer library on one MI355X.
+
+One step = one jm_mixer_prefill call over the 4K-token Jamba-v0.1 prefill (B=1, L=4096, d_inner=8192,
+d_state=16, dt_rank=256, bf16 I/O, fp32 state), i.e. every step of the mixer: conv1d + SiLU, x_proj,
+the dt/B/C RMSNorms, dt_proj + softplus, the selective scan, the D skip and the SiLU(z) gate.  Inputs are
+seeded synthetic tensors already resident in HBM.  W untimed warmup steps, then K timed steps between
+device synchronisations; value = tokens / second.  A second timed pass records HIP events between the
+library's kernels (jm_mixer_prefill_profiled) for the per-kernel roofline.  The decode workload (B=256,
+one token per sequence, the fp32 state rotated over 4 sets so that it streams from HBM) is timed the same
+way and reported alongside.  The fp64 CPU oracle is timed on the host on the same prefill workload as a
+baseline.
+
+Prints one JSON line.  Only one GPU is supported: --gpus N with N > 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+N_STATE_SETS = 4               # decode state sets rotated per step (4 x 140 MB > the 256 MB last-level cache)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent_t handles through the HIP runtime the process already uses (torch's)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(e)
+
+
+def algorithmic_bytes(B, L, C, N, R, esize):
+    """Fixed per-stage byte counts (what each step must move at minimum, in the I/O precision):
+    conv: x in, xc out; x_proj: xc in, dbc out (fp32), W_x once; norm + dt_proj: dbc in, delta out,
+    B/C out (fp32), W_dt once; scan + gate: xc, delta, z in, B/C in, out, SSM state in and out (fp32)."""
+    T = B * L
+    W = R + 2 * N
+    return {
+        "conv_silu": T * C * 2 * esize + C * 5 * esize,
+        "x_proj": T * C * esize + T * W * 4 + W * C * esize,
+        "norm_dt_proj": T * W * 4 + T * C * esize + T * 2 * N * 4 + C * R * esize + C * esize,
+        "scan_gate": T * C * 4 * esize + T * 2 * N * 4 + 2 * B * C * N * 4 + C * (N + 1) * esize,
+    }
+
+
+def decode_bytes(B, C, N, R, K, esize):
+    """One decode step: per (sequence, channel) the fp32 state in and out, the conv state in and out, x and z
+    in, out; plus every weight once."""
+    W = R + 2 * N
+    per = 2 * N * 4 + 2 * (K - 1) * esize + 3 * esize
+    weights = (C * K + C + W * C + R + 2 * N + C * R + C + C * N + C) * esize
+    return B * C * per + weights
+
+
+def stage_groups(stage_ms):
+    return {
+        "conv_silu": stage_ms["conv_silu"],
+        "x_proj": stage_ms["x_proj"],
+        "norm_dt_proj": stage_ms["norm"] + stage_ms["dt_proj"],
+        "scan_gate": stage_ms["scan_local"] + stage_ms["scan_carry"] + stage_ms["scan_full"],
+    }
+
+
+def time_prefill(jm, cfg, steps, warmup, hip):
+    import torch
+    from jm_inputs import make_activations, make_weights
+
+    dev = "cuda"
+    w = make_weights(cfg, dev)
+    a = make_activations(cfg, dev)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    B, L, C = cfg.batch, cfg.seqlen, cfg.d_inner
+    out = torch.empty((B, L, C), dtype=cfg.torch_dtype, device=dev)
+    cs = torch.empty((B, C, cfg.d_conv - 1), dtype=cfg.torch_dtype, device=dev)
+    hs = torch.empty((B, C, cfg.d_state), dtype=torch.float32, device=dev)
+    dims = m.dims(B, L)
+    ws = m.workspace(jm.prefill_workspace_size(dims))
+    stream = torch.cuda.current_stream().cuda_stream
+    x, z = a["x"], a["z"]
+
+    def step():
+        s = jm.call_prefill(dims, m.packed, x.data_ptr(), z.data_ptr(), out.data_ptr(), None, cs.data_ptr(), None,
+                            hs.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_mixer_prefill")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+
+    # per-stage pass
+    nst = 7
+    names = [jm.lib().jm_stage_name(i).decode() for i in range(nst)]
+    evs = hip.events(steps * (nst + 1))
+    arr_t = ctypes.c_void_p * (nst + 1)
+    L_ = jm.lib()
+    L_.jm_mixer_prefill_profiled.restype = ctypes.c_int
+    for k in range(steps):
+        arr = arr_t(*[e.value for e in evs[k * (nst + 1):(k + 1) * (nst + 1)]])
+        s = L_.jm_mixer_prefill_profiled(ctypes.byref(dims), ctypes.byref(m.packed), ctypes.c_void_p(x.data_ptr()),
+                                         ctypes.c_void_p(z.data_ptr()), ctypes.c_void_p(out.data_ptr()), None,
+                                         ctypes.c_void_p(cs.data_ptr()), None, ctypes.c_void_p(hs.data_ptr()),
+                                         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                                         ctypes.c_void_p(stream), arr, ctypes.c_int(nst + 1))
+        if s != 0:
+            raise jm.JMError(s, "jm_mixer_prefill_profiled")
+    torch.cuda.synchronize()
+    stage_ms = {n: 0.0 for n in names}
+    for k in range(steps):
+        base = k * (nst + 1)
+        for i, n in enumerate(names):
+            stage_ms[n] += hip.elapsed_ms(evs[base + i], evs[base + i + 1]) / steps
+    hip.destroy(evs)
+    lay = jm.workspace_layout(dims)
+    return {"ms": ms, "wall_s": wall, "stage_ms": stage_ms, "splits": lay.dbc_splits, "pieces": lay.scan_chunks}
+
+
+def time_decode(jm, cfg, steps, warmup, hip):
+    import torch
+    from jm_inputs import make_state, make_weights
+
+    dev = "cuda"
+    w = make_weights(cfg, dev)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    B, C = cfg.batch, cfg.d_inner
+    st = make_state(cfg, dev)
+    sets = [(st["conv_state"].clone(), st["ssm_state"].clone()) for _ in range(N_STATE_SETS)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    xs = torch.randn((8, B, C), generator=g, device=dev).to(cfg.torch_dtype)
+    zs = torch.randn((8, B, C), generator=g, device=dev).to(cfg.torch_dtype)
+    out = torch.empty((B, C), dtype=cfg.torch_dtype, device=dev)
+    dims = m.dims(B, 1)
+    ws = m.workspace(jm.decode_workspace_size(dims))
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        c, h = sets[i % N_STATE_SETS]
+        s = jm.call_decode_step(dims, m.packed, xs[i % 8].data_ptr(), zs[i % 8].data_ptr(), out.data_ptr(),
+                                c.data_ptr(), c.data_ptr(), h.data_ptr(), h.data_ptr(), ws.data_ptr(), ws.numel(),
+                                stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_mixer_decode_step")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+
+    nst = 7
+    names = [jm.lib().jm_stage_name(i).decode() for i in range(nst)]
+    evs = hip.events(steps * (nst + 1))
+    arr_t = ctypes.c_void_p * (nst + 1)
+    L_ = jm.lib()
+    for k in range(steps):
+        c, h = sets[k % N_STATE_SETS]
+        arr = arr_t(*[e.value for e in evs[k * (nst + 1):(k + 1) * (nst + 1)]])
+        s = L_.jm_mixer_decode_step_profiled(
+            ctypes.byref(dims), ctypes.byref(m.packed), ctypes.c_void_p(xs[k % 8].data_ptr()),
+            ctypes.c_void_p(zs[k % 8].data_ptr()), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(c.data_ptr()),
+            ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(h.data_ptr()), ctypes.c_void_p(h.data_ptr()),
+            ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream), arr,
+            ctypes.c_int(nst + 1))
+        if s != 0:
+            raise jm.JMError(s, "jm_mixer_decode_step_profiled")
+    torch.cuda.synchronize()
+    stage_ms = {n: 0.0 for n in names}
+    for k in range(steps):
+        base = k * (nst + 1)
+        for i, n in enumerate(names):
+            stage_ms[n] += hip.elapsed_ms(evs[base + i], evs[base + i + 1]) / steps
+    hip.destroy(evs)
+    return {"ms": ms, "stage_ms": stage_ms}
+
+
+def cpu_baseline(cfg, max_tokens):
+    """The fp64 oracle (as it stands) on the host cores: the first max_tokens tokens of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from jm_inputs import make_activations, make_weights, to_f64
+
+    w = {k: to_f64(v) for k, v in make_weights(cfg).items()}
+    a = make_activations(cfg, "cpu")
+    L = min(cfg.seqlen, max_tokens)
+    x, z = to_f64(a["x"][:, :L]), to_f64(a["z"][:, :L])
+    t0 = time.perf_counter()
+    out, _, _ = oracle.mixer_prefill(x, z, w, cfg.dt_rank, cfg.d_state, cfg.norm_eps)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": cfg.batch * L / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, prefill of the first {L} tokens of {cfg.name} (B={cfg.batch}, "
+                      f"C={cfg.d_inner}), {dt:.1f} s; matmuls on {blas} BLAS threads, the scan single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_selective_scan_05_amd as jm
+    from jm_inputs import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    jm.lib()
+    hip = Hip()
+    cfg = CONFIGS[1]
+    log(f"prefill {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+    pre = time_prefill(jm, cfg, args.steps, args.warmup, hip)
+    B, L, C, N, R = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dt_rank
+    tokens = B * L
+    value = tokens / (pre["ms"] * 1e-3)
+    alg = algorithmic_bytes(B, L, C, N, R, 2)
+    groups = stage_groups(pre["stage_ms"])
+    stages = {}
+    for k, t in groups.items():
+        gbs = alg[k] / (t * 1e-3) / 1e9 if t > 0 else 0.0
+        stages[k] = {"us": round(t * 1e3, 2), "alg_bytes": alg[k], "GB_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    for k, t in pre["stage_ms"].items():
+        log(f"  {k:12s} {t * 1e3:9.2f} us")
+    dom = max(groups, key=lambda k: groups[k])
+    ach = stages[dom]["GB_s"]
+    xflops = 2.0 * tokens * (R + 2 * N) * C
+    stages["x_proj"]["mfma_tflops"] = round(xflops / (groups["x_proj"] * 1e-3) / 1e12, 2)
+    stages["x_proj"]["frac_mfma_bf16"] = round(stages["x_proj"]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    result = {
+        "metric": "mixer tokens/sec at d_inner=8192 (prefill & decode); achieved HBM GB/s % peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Jamba-v0.1 Mamba mixer prefill", "batch": B, "seq_len": L,
+                   "d_inner": C, "d_state": N, "dt_rank": R, "d_conv": cfg.d_conv, "io": "bf16",
+                   "state": "fp32", "x_proj_splits": pre["splits"], "scan_pieces": pre["pieces"]},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "stages": stages,
+        "mixer_GB_s": round(sum(alg.values()) / (pre["ms"] * 1e-3) / 1e9, 1),
+    }
+    if not args.no_decode:
+        dcfg = CONFIGS[4]
+        log(f"decode {dcfg.name}: warmup {args.warmup}, steps {args.steps}")
+        dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
+        db = decode_bytes(dcfg.batch, dcfg.d_inner, dcfg.d_state, dcfg.dt_rank, dcfg.d_conv, 2)
+        gbs = db / (dec["ms"] * 1e-3) / 1e9
+        for k, t in dec["stage_ms"].items():
+            log(f"  {k:12s} {t * 1e3:9.2f} us")
+        result["decode"] = {"workload": f"{dcfg.name}: one token per sequence, state rotated over {N_STATE_SETS} sets",
+                            "batch": dcfg.batch, "us_per_step": round(dec["ms"] * 1e3, 2),
+                            "tokens_per_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "alg_bytes": db,
+                            "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()}}
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {min(args.cpu_tokens, cfg.seqlen)} tokens ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

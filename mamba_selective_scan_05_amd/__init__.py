@@ -1,0 +1,9 @@
+"""Jamba's Mamba-1 mixer (conv1d + SiLU, x_proj, dt/B/C RMSNorms, dt_proj + softplus, selective scan, D skip,
+SiLU(z) gate) as hand-written HIP kernels for AMD MI355X (gfx950), behind the C ABI of include/jm_mixer.h.
+
+``Mixer`` wraps the two entry points (``jm_mixer_prefill``, ``jm_mixer_decode_step``) on torch tensors.
+"""
+
+from ._lib import (JM_BF16, JM_F32, JMError, Mixer, Dims, Weights, WorkspaceLayout, call_decode_step,  # noqa: F401
+                   call_prefill, decode_workspace_size, lib, make_dims, pack_weights, prefill_workspace_size,
+                   status_string, workspace_layout)

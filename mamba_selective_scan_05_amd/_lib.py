@@ -1,0 +1,234 @@
+"""ctypes binding of libjm_mixer.so (the C ABI in include/jm_mixer.h).
+
+The functions here only marshal arguments: torch tensors provide device memory and the stream, their
+data pointers go to the library, and every step of the mixer runs in the library's HIP kernels.  If the
+library is missing, loading fails loudly; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libjm_mixer.so")
+
+JM_OK, JM_ERR_INVALID_ARG, JM_ERR_UNSUPPORTED, JM_ERR_ALIGNMENT, JM_ERR_WORKSPACE, JM_ERR_HIP = 0, -1, -2, -3, -4, -5
+JM_F32, JM_BF16 = 0, 1
+
+WEIGHT_NAMES = ("conv_w", "conv_b", "x_proj_w", "dt_norm_w", "b_norm_w", "c_norm_w", "dt_proj_w", "dt_proj_b",
+                "A_log", "D")
+
+
+class JMError(RuntimeError):
+    """A nonzero status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("d_inner", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("dt_rank", ctypes.c_int32), ("d_conv", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("x_row_stride", ctypes.c_int64), ("z_row_stride", ctypes.c_int64)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("xc", ctypes.c_int64), ("dbc", ctypes.c_int64), ("dln", ctypes.c_int64), ("bc", ctypes.c_int64),
+                ("delta", ctypes.c_int64), ("carries", ctypes.c_int64), ("dbc_splits", ctypes.c_int32),
+                ("scan_chunks", ctypes.c_int32), ("total_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built by ``python -m mamba_selective_scan_05_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mamba_selective_scan_05_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, V, I, S = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        for name in ("jm_mixer_prefill", "jm_mixer_decode_step"):
+            f = getattr(L, name)
+            f.argtypes = [P(Dims), P(Weights), V, V, V, V, V, V, V, V, S, V]
+            f.restype = I
+        for name in ("jm_mixer_prefill_workspace_size", "jm_mixer_decode_workspace_size"):
+            f = getattr(L, name)
+            f.argtypes = [P(Dims)]
+            f.restype = S
+        L.jm_status_string.argtypes = [I]
+        L.jm_status_string.restype = ctypes.c_char_p
+        L.jm_mixer_prefill_workspace_layout.argtypes = [P(Dims), P(WorkspaceLayout)]
+        L.jm_mixer_prefill_workspace_layout.restype = I
+        for name in ("jm_mixer_prefill_profiled", "jm_mixer_decode_step_profiled"):
+            f = getattr(L, name)
+            f.argtypes = [P(Dims), P(Weights), V, V, V, V, V, V, V, V, S, V, P(V), I]
+            f.restype = I
+        L.jm_stage_name.argtypes = [I]
+        L.jm_stage_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().jm_status_string(status).decode()
+
+
+def make_dims(batch: int, seqlen: int, d_inner: int, dt_rank: int, io_dtype: int, d_state: int = 16,
+              d_conv: int = 4, norm_eps: float = 1e-6, x_row_stride: int = 0, z_row_stride: int = 0) -> Dims:
+    return Dims(batch, seqlen, d_inner, d_state, dt_rank, d_conv, io_dtype, norm_eps, x_row_stride, z_row_stride)
+
+
+def prefill_workspace_size(dims: Dims) -> int:
+    return int(lib().jm_mixer_prefill_workspace_size(ctypes.byref(dims)))
+
+
+def decode_workspace_size(dims: Dims) -> int:
+    return int(lib().jm_mixer_decode_workspace_size(ctypes.byref(dims)))
+
+
+def workspace_layout(dims: Dims) -> WorkspaceLayout:
+    lay = WorkspaceLayout()
+    s = lib().jm_mixer_prefill_workspace_layout(ctypes.byref(dims), ctypes.byref(lay))
+    if s != JM_OK:
+        raise JMError(s, "jm_mixer_prefill_workspace_layout")
+    return lay
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def pack_weights(w: Dict[str, torch.Tensor]) -> Weights:
+    return Weights(*[_ptr(w.get(n)) for n in WEIGHT_NAMES])
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def call_prefill(dims: Dims, weights: Weights, x, z, out, conv_in, conv_out, h_in, h_out, ws, ws_bytes: int,
+                 stream: int) -> int:
+    """The raw entry point on integer device pointers (None for NULL)."""
+    return lib().jm_mixer_prefill(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in, h_out, ws,
+                                  ws_bytes, stream)
+
+
+def call_decode_step(dims: Dims, weights: Weights, x, z, out, conv_in, conv_out, h_in, h_out, ws, ws_bytes: int,
+                     stream: int) -> int:
+    return lib().jm_mixer_decode_step(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in, h_out, ws,
+                                      ws_bytes, stream)
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return JM_F32
+    if t.dtype == torch.bfloat16:
+        return JM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _row_stride(t: torch.Tensor, rows_per_batch: int) -> int:
+    """Row stride of a [B, L, C] (or [B, C]) view whose channel dim is contiguous and whose rows are evenly
+    spaced across the batch."""
+    if t.stride(-1) != 1:
+        raise ValueError("the channel dimension must be contiguous")
+    rs = t.stride(-2) if t.dim() == 3 else t.stride(0)
+    if t.dim() == 3 and t.shape[0] > 1 and t.stride(0) != rows_per_batch * rs:
+        raise ValueError("rows must be evenly spaced across the batch")
+    return int(rs)
+
+
+def _check_contiguous(**tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Mixer:
+    """Holds the weights (device tensors in the I/O dtype) and a reusable workspace."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], dt_rank: int, d_state: int = 16, d_conv: int = 4,
+                 norm_eps: float = 1e-6):
+        self.w = {k: v.contiguous() for k, v in weights.items()}
+        self.packed = pack_weights(self.w)
+        self.dt_rank, self.d_state, self.d_conv, self.eps = dt_rank, d_state, d_conv, norm_eps
+        self.d_inner = self.w["conv_w"].shape[0]
+        self.device = self.w["conv_w"].device
+        self.dtype = self.w["conv_w"].dtype
+        self._ws = None
+
+    def dims(self, batch: int, seqlen: int, x_row_stride: int = 0, z_row_stride: int = 0) -> Dims:
+        return make_dims(batch, seqlen, self.d_inner, self.dt_rank, _io_dtype(self.w["conv_w"]), self.d_state,
+                         self.d_conv, self.eps, x_row_stride, z_row_stride)
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def prefill(self, x: torch.Tensor, z: torch.Tensor, conv_state: Optional[torch.Tensor] = None,
+                ssm_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                conv_state_out: Optional[torch.Tensor] = None, ssm_state_out: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        B, L, C = x.shape
+        dims = self.dims(B, L, _row_stride(x, L), _row_stride(z, L))
+        nbytes = prefill_workspace_size(dims)
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_mixer_prefill_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.empty((B, L, C), dtype=self.dtype, device=self.device)
+        if conv_state_out is None:
+            conv_state_out = torch.empty((B, C, self.d_conv - 1), dtype=self.dtype, device=self.device)
+        if ssm_state_out is None:
+            ssm_state_out = torch.empty((B, C, self.d_state), dtype=torch.float32, device=self.device)
+        _check_contiguous(out=out, conv_state=conv_state, conv_state_out=conv_state_out, ssm_state=ssm_state,
+                          ssm_state_out=ssm_state_out)
+        s = call_prefill(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_state), _ptr(conv_state_out),
+                         _ptr(ssm_state), _ptr(ssm_state_out), _ptr(ws), ws.numel(), _stream(self.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_mixer_prefill")
+        return out, conv_state_out, ssm_state_out
+
+    def decode_step(self, x: torch.Tensor, z: torch.Tensor, conv_state: torch.Tensor, ssm_state: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None,
+                    ssm_state_out: Optional[torch.Tensor] = None, in_place: bool = False
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """One token per sequence: x, z are [B, C].  With in_place=True the states are updated in place."""
+        B, C = x.shape
+        dims = self.dims(B, 1, _row_stride(x, 1), _row_stride(z, 1))
+        nbytes = decode_workspace_size(dims)
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_mixer_decode_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.empty((B, C), dtype=self.dtype, device=self.device)
+        if in_place:
+            conv_state_out, ssm_state_out = conv_state, ssm_state
+        if conv_state_out is None:
+            conv_state_out = torch.empty_like(conv_state)
+        if ssm_state_out is None:
+            ssm_state_out = torch.empty_like(ssm_state)
+        _check_contiguous(out=out, conv_state=conv_state, conv_state_out=conv_state_out, ssm_state=ssm_state,
+                          ssm_state_out=ssm_state_out)
+        s = call_decode_step(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_state), _ptr(conv_state_out),
+                             _ptr(ssm_state), _ptr(ssm_state_out), _ptr(ws), ws.numel(), _stream(self.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_mixer_decode_step")
+        return out, conv_state_out, ssm_state_out

@@ -1,0 +1,65 @@
+// Device-side helpers shared by the mixer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jm {
+
+typedef uint16_t bf16_t;
+
+// bf16 <-> fp32.  Widening is exact (the bf16 bits are the high half of the fp32); narrowing rounds to
+// nearest-even through the hardware converter (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct io;
+template <> struct io<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float cvt(float v) { return v; }
+  static __device__ __forceinline__ float from(float v) { return v; }
+};
+template <> struct io<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+  static __device__ __forceinline__ float cvt(bf16_t v) { return bf2f(v); }
+  static __device__ __forceinline__ bf16_t from(float v) { return f2bf(v); }
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x on the transcendental unit (v_exp_f32, about 1 ulp; flushes to 0 far below the normal range).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// 1/x on the transcendental unit (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// SiLU(u) = u / (1 + e^-u).  For u -> -inf the exp overflows to inf and the reciprocal gives 0.
+__device__ __forceinline__ float silu(float u) { return u * rcp_fast(1.0f + exp2_fast(-u * kLog2e)); }
+
+// log(1 + e) for e in [0, 1], accurate to a few ulp also for tiny e: the rounding of 1 + e is undone by
+// scaling log(u) with e / (u - 1) (the standard correction for log1p).
+__device__ __forceinline__ float log1p_small(float e) {
+  float u = 1.0f + e;
+  float d = u - 1.0f;
+  float l = __builtin_amdgcn_logf(u) * kLn2;  // v_log_f32 is log2
+  return d == 0.0f ? e : l * (e / d);
+}
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|), without overflow.
+__device__ __forceinline__ float softplus(float v) {
+  float e = exp2_fast(-fabsf(v) * kLog2e);
+  return fmaxf(v, 0.0f) + log1p_small(e);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace jm

@@ -1,0 +1,53 @@
+// Host-side launchers of the mixer kernels (internal to the library; the public ABI is jm_mixer.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jm {
+
+// Causal depthwise conv1d (K = 4) + bias + SiLU over [B, L, C] -> xc [B*L, C] (contiguous).
+void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
+                      const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
+
+// dbc partial sums: part[s, m, n] = sum over channel slice s of xc[m, k] * w[n, k].
+void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
+                  hipStream_t st);
+
+// Sum the partials in slice order, RMSNorm the dt / B / C slices -> dln [M, R] (io dtype), bc [M, 2N].
+void launch_norm(bool bf16, const float* part, int splits, int M, int R, int N, const void* dt_norm_w,
+                 const void* b_norm_w, const void* c_norm_w, float eps, void* dln, float* bc, hipStream_t st);
+
+// delta[m, c] = softplus(sum_r dln[m, r] * w[c, r] + b[c])  (io dtype).
+void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, void* delta, int M, int C, int R,
+                   hipStream_t st);
+
+struct ScanArgs {
+  const void* xc;        // [B*L, C] io dtype
+  const void* delta;     // [B*L, C] io dtype
+  const void* z;         // [B*L rows, z_stride]
+  int64_t z_stride;
+  const float* bc;       // [B*L, 2N]
+  const void* A_log;     // [C, N]
+  const void* D;         // [C]
+  const float* h0;       // [B, C, N] or null
+  void* out;             // [B*L, C]
+  float* h_out;          // [B, C, N]
+  const void* x;         // raw input, for the conv state
+  int64_t x_stride;
+  const void* conv_in;   // [B, C, K-1] or null
+  void* conv_out;        // [B, C, K-1]
+  float* loc;            // [B, P, N+1, C]   per-piece local end states and dt sums (P > 1)
+  float* cin;            // [B, P, N, C]     per-piece incoming states (P > 1)
+  int B, L, C, P, Lp;
+};
+
+// The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.
+// marks (optional): events recorded before the local pass, the carry pass and the full pass.
+void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks = nullptr);
+
+// seqlen == 0: copy the states through (zeros for a NULL input).
+void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,
+                              int B, int C, hipStream_t st);
+
+}  // namespace jm

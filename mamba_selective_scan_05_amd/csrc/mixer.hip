@@ -1,0 +1,273 @@
+// The library's C ABI (jm_mixer.h): argument checks, the execution plan, the workspace layout, and the
+// kernel sequence on the caller's stream.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "jm_launch.h"
+#include "jm_mixer.h"
+
+namespace {
+
+constexpr int kN = 16;       // d_state the kernels are built for
+constexpr int kTaps = 4;     // d_conv the kernels are built for
+constexpr int kMaxR = 512;   // dt_rank bound of the norm kernel
+constexpr int64_t kAlign = 256;
+
+// Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.
+constexpr int64_t kScanWaveTarget = 2048;
+constexpr int kMinPiece = 256;
+// x_proj: aim for at least this many workgroups before splitting the contraction over channel slices.
+constexpr int kXprojWgTarget = 512;
+
+struct Plan {
+  int B, L, C, N, R, W;
+  int64_t T;
+  bool bf16;
+  int esize;
+  int splits;    // x_proj channel slices
+  int P, Lp;     // scan pieces per sequence, tokens per piece
+  int64_t xs, zs;
+  int64_t off_xc, off_dbc, off_dln, off_bc, off_delta, off_loc, off_cin, total;
+};
+
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_dims(const jm_mixer_dims* d, bool decode) {
+  if (!d) return JM_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->d_inner < 1 || d->dt_rank < 1) return JM_ERR_INVALID_ARG;
+  if (!decode && d->seqlen < 0) return JM_ERR_INVALID_ARG;
+  if (!(d->norm_eps >= 0.0f)) return JM_ERR_INVALID_ARG;
+  if (d->io_dtype != JM_F32 && d->io_dtype != JM_BF16) return JM_ERR_UNSUPPORTED;
+  if (d->d_state != kN || d->d_conv != kTaps) return JM_ERR_UNSUPPORTED;
+  if (d->d_inner % 64 != 0) return JM_ERR_UNSUPPORTED;
+  if (d->dt_rank > kMaxR || d->dt_rank % 8 != 0) return JM_ERR_UNSUPPORTED;
+  const int64_t xs = d->x_row_stride ? d->x_row_stride : d->d_inner;
+  const int64_t zs = d->z_row_stride ? d->z_row_stride : d->d_inner;
+  if (xs < d->d_inner || zs < d->d_inner) return JM_ERR_INVALID_ARG;
+  if (xs % 8 != 0 || zs % 8 != 0) return JM_ERR_ALIGNMENT;
+  return JM_OK;
+}
+
+Plan make_plan(const jm_mixer_dims* d, bool decode) {
+  Plan p;
+  p.B = d->batch;
+  p.L = decode ? 1 : d->seqlen;
+  p.C = d->d_inner;
+  p.N = d->d_state;
+  p.R = d->dt_rank;
+  p.W = p.R + 2 * p.N;
+  p.T = (int64_t)p.B * p.L;
+  p.bf16 = d->io_dtype == JM_BF16;
+  p.esize = p.bf16 ? 2 : 4;
+  p.xs = d->x_row_stride ? d->x_row_stride : p.C;
+  p.zs = d->z_row_stride ? d->z_row_stride : p.C;
+
+  // x_proj split: channel slices of a multiple of 64, dividing C, until the grid is big enough.
+  p.splits = 1;
+  if (p.bf16) {
+    const int64_t mtiles = (p.T + 63) / 64;
+    while (mtiles * p.splits < kXprojWgTarget && (p.C / 64) % (p.splits * 2) == 0) p.splits *= 2;
+  }
+
+  // scan pieces
+  const int64_t waves = (int64_t)p.B * (p.C / 64);
+  int64_t want = (kScanWaveTarget + waves - 1) / waves;
+  int64_t lp = p.L > 0 ? (p.L + want - 1) / want : 1;
+  if (lp < kMinPiece) lp = kMinPiece;
+  p.Lp = (int)(lp < p.L ? lp : (p.L > 0 ? p.L : 1));
+  p.P = p.L > 0 ? (int)((p.L + p.Lp - 1) / p.Lp) : 1;
+
+  int64_t off = 0;
+  p.off_xc = off;    off += align_up(p.T * p.C * p.esize);
+  p.off_dbc = off;   off += align_up((int64_t)p.splits * p.T * p.W * 4);
+  p.off_dln = off;   off += align_up(p.T * p.R * p.esize);
+  p.off_bc = off;    off += align_up(p.T * 2 * p.N * 4);
+  p.off_delta = off; off += align_up(p.T * p.C * p.esize);
+  if (p.P > 1) {
+    p.off_loc = off; off += align_up((int64_t)p.B * p.P * (p.N + 1) * p.C * 4);
+    p.off_cin = off; off += align_up((int64_t)p.B * p.P * p.N * p.C * 4);
+  } else {
+    p.off_loc = p.off_cin = -1;
+  }
+  p.total = off > 0 ? off : kAlign;
+  return p;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_weights(const jm_mixer_weights* w) {
+  if (!w) return JM_ERR_INVALID_ARG;
+  const void* req[] = {w->conv_w, w->x_proj_w, w->dt_norm_w, w->b_norm_w, w->c_norm_w,
+                       w->dt_proj_w, w->dt_proj_b, w->A_log, w->D};
+  for (const void* q : req)
+    if (!q) return JM_ERR_INVALID_ARG;
+  for (const void* q : req)
+    if (!aligned16(q)) return JM_ERR_ALIGNMENT;
+  if (w->conv_b && !aligned16(w->conv_b)) return JM_ERR_ALIGNMENT;
+  return JM_OK;
+}
+
+const char* const kStageNames[JM_STAGES] = {"conv_silu", "x_proj", "norm", "dt_proj", "scan_local",
+                                            "scan_carry", "scan_full"};
+
+// Records events[i] before stage i when per-stage timing was asked for.
+struct StageMarks {
+  void** ev;
+  hipStream_t st;
+  void mark(int i) const {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], st);
+  }
+};
+
+int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+        const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+        void* stream, bool decode, void** events = nullptr, int n_events = 0) {
+  int s = check_dims(dims, decode);
+  if (s != JM_OK) return s;
+  if ((s = check_weights(w)) != JM_OK) return s;
+  const Plan p = make_plan(dims, decode);
+  if (!conv_out || !h_out) return JM_ERR_INVALID_ARG;
+  if (decode && (!conv_in || !h0)) return JM_ERR_INVALID_ARG;
+  if (p.L > 0 && (!x || !z || !out)) return JM_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, z, out, conv_in, conv_out, h0, h_out, ws};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return JM_ERR_ALIGNMENT;
+  if (!ws || (int64_t)ws_bytes < p.total) return JM_ERR_WORKSPACE;
+  if (events) {
+    if (n_events < JM_STAGES + 1) return JM_ERR_INVALID_ARG;
+    for (int i = 0; i <= JM_STAGES; ++i)
+      if (!events[i]) return JM_ERR_INVALID_ARG;
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  const StageMarks marks{events, st};
+  (void)hipGetLastError();  // clear a stale error so the check below reports this call's launches only
+  if (p.L == 0) {
+    marks.mark(0);
+    jm::launch_state_passthrough(p.bf16, conv_in, conv_out, h0, h_out, p.B, p.C, st);
+    for (int i = 1; i <= JM_STAGES; ++i) marks.mark(i);
+    return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
+  }
+  char* base = (char*)ws;
+  void* xc = base + p.off_xc;
+  float* dbc = (float*)(base + p.off_dbc);
+  void* dln = base + p.off_dln;
+  float* bc = (float*)(base + p.off_bc);
+  void* delta = base + p.off_delta;
+
+  marks.mark(0);
+  jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st);
+  marks.mark(1);
+  jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, st);
+  marks.mark(2);
+  jm::launch_norm(p.bf16, dbc, p.splits, (int)p.T, p.R, p.N, w->dt_norm_w, w->b_norm_w, w->c_norm_w,
+                  dims->norm_eps, dln, bc, st);
+  marks.mark(3);
+  jm::launch_dtproj(p.bf16, dln, w->dt_proj_w, w->dt_proj_b, delta, (int)p.T, p.C, p.R, st);
+  marks.mark(4);
+  jm::ScanArgs a;
+  a.xc = xc;
+  a.delta = delta;
+  a.z = z;
+  a.z_stride = p.zs;
+  a.bc = bc;
+  a.A_log = w->A_log;
+  a.D = w->D;
+  a.h0 = h0;
+  a.out = out;
+  a.h_out = h_out;
+  a.x = x;
+  a.x_stride = p.xs;
+  a.conv_in = conv_in;
+  a.conv_out = conv_out;
+  a.loc = p.P > 1 ? (float*)(base + p.off_loc) : nullptr;
+  a.cin = p.P > 1 ? (float*)(base + p.off_cin) : nullptr;
+  a.B = p.B;
+  a.L = p.L;
+  a.C = p.C;
+  a.P = p.P;
+  a.Lp = p.Lp;
+  jm::launch_scan(p.bf16, a, st, events ? &marks.ev[5] : nullptr);
+  marks.mark(JM_STAGES);
+  return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t jm_mixer_prefill_workspace_size(const jm_mixer_dims* dims) {
+  if (check_dims(dims, false) != JM_OK) return 0;
+  return (size_t)make_plan(dims, false).total;
+}
+
+size_t jm_mixer_decode_workspace_size(const jm_mixer_dims* dims) {
+  if (check_dims(dims, true) != JM_OK) return 0;
+  return (size_t)make_plan(dims, true).total;
+}
+
+int jm_mixer_prefill(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x, const void* z,
+                     void* out, const void* conv_state_in, void* conv_state_out, const float* ssm_state_in,
+                     float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
+             workspace_bytes, stream, false);
+}
+
+int jm_mixer_decode_step(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x, const void* z,
+                         void* out, const void* conv_state_in, void* conv_state_out, const float* ssm_state_in,
+                         float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
+             workspace_bytes, stream, true);
+}
+
+int jm_mixer_prefill_profiled(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
+                              const void* z, void* out, const void* conv_state_in, void* conv_state_out,
+                              const float* ssm_state_in, float* ssm_state_out, void* workspace,
+                              size_t workspace_bytes, void* stream, void** events, int n_events) {
+  if (!events) return JM_ERR_INVALID_ARG;
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
+             workspace_bytes, stream, false, events, n_events);
+}
+
+int jm_mixer_decode_step_profiled(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
+                                  const void* z, void* out, const void* conv_state_in, void* conv_state_out,
+                                  const float* ssm_state_in, float* ssm_state_out, void* workspace,
+                                  size_t workspace_bytes, void* stream, void** events, int n_events) {
+  if (!events) return JM_ERR_INVALID_ARG;
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
+             workspace_bytes, stream, true, events, n_events);
+}
+
+const char* jm_stage_name(int stage) { return stage >= 0 && stage < JM_STAGES ? kStageNames[stage] : "?"; }
+
+int jm_mixer_prefill_workspace_layout(const jm_mixer_dims* dims, jm_workspace_layout* layout) {
+  if (!layout) return JM_ERR_INVALID_ARG;
+  const int s = check_dims(dims, false);
+  if (s != JM_OK) return s;
+  const Plan p = make_plan(dims, false);
+  layout->xc = p.off_xc;
+  layout->dbc = p.off_dbc;
+  layout->dln = p.off_dln;
+  layout->bc = p.off_bc;
+  layout->delta = p.off_delta;
+  layout->carries = p.off_loc;
+  layout->dbc_splits = p.splits;
+  layout->scan_chunks = p.P;
+  layout->total_bytes = p.total;
+  return JM_OK;
+}
+
+const char* jm_status_string(int status) {
+  switch (status) {
+    case JM_OK: return "ok";
+    case JM_ERR_INVALID_ARG: return "invalid argument (NULL required pointer, bad size or stride)";
+    case JM_ERR_UNSUPPORTED: return "unsupported dims or dtype (d_state must be 16, d_conv 4, d_inner % 64 == 0, "
+                                    "dt_rank a multiple of 8 up to 512)";
+    case JM_ERR_ALIGNMENT: return "misaligned pointer (16 bytes required) or row stride (multiple of 8)";
+    case JM_ERR_WORKSPACE: return "workspace missing or too small";
+    case JM_ERR_HIP: return "HIP runtime error while enqueueing a kernel";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

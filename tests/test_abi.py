@@ -1,0 +1,114 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects bad arguments on the
+host before anything is enqueued (no GPU is touched by these tests)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_selective_scan_05_amd as jm
+from mamba_selective_scan_05_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jm_mixer.h")
+
+FAKE = 0x10000          # 16-byte aligned stand-in pointer; never dereferenced because validation fails first
+WS_BIG = 1 << 40
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(jm_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"jm_mixer_prefill", "jm_mixer_decode_step", "jm_mixer_prefill_workspace_size",
+            "jm_mixer_decode_workspace_size", "jm_status_string"} <= set(names)
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _dims(**kw):
+    d = dict(batch=1, seqlen=64, d_inner=64, dt_rank=8, io_dtype=jm.JM_F32)
+    d.update(kw)
+    return jm.make_dims(**d)
+
+
+def _weights(**override):
+    w = {n: FAKE for n in _lib.WEIGHT_NAMES}
+    w.update(override)
+    return jm.Weights(*[w[n] for n in _lib.WEIGHT_NAMES])
+
+
+def _call(dims, weights=None, decode=False, **ptr):
+    p = dict(x=FAKE, z=FAKE, out=FAKE, conv_in=FAKE, conv_out=FAKE, h_in=FAKE, h_out=FAKE, ws=FAKE, ws_bytes=WS_BIG)
+    p.update(ptr)
+    f = jm.call_decode_step if decode else jm.call_prefill
+    return f(dims, weights or _weights(), p["x"], p["z"], p["out"], p["conv_in"], p["conv_out"], p["h_in"],
+             p["h_out"], p["ws"], p["ws_bytes"], 0)
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_validation_rejects_bad_arguments_before_launch(decode):
+    E = _lib
+    assert _call(_dims(d_state=8), decode=decode) == E.JM_ERR_UNSUPPORTED
+    assert _call(_dims(d_conv=3), decode=decode) == E.JM_ERR_UNSUPPORTED
+    assert _call(_dims(d_inner=96), decode=decode) == E.JM_ERR_UNSUPPORTED
+    assert _call(_dims(dt_rank=12), decode=decode) == E.JM_ERR_UNSUPPORTED
+    assert _call(_dims(dt_rank=520), decode=decode) == E.JM_ERR_UNSUPPORTED
+    assert _call(_dims(io_dtype=7), decode=decode) == E.JM_ERR_UNSUPPORTED
+    assert _call(_dims(batch=0), decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(_dims(norm_eps=-1.0), decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(_dims(x_row_stride=32), decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(_dims(z_row_stride=68), decode=decode) == E.JM_ERR_ALIGNMENT
+    assert _call(_dims(), _weights(A_log=None), decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(_dims(), _weights(D=FAKE + 4), decode=decode) == E.JM_ERR_ALIGNMENT
+    assert _call(_dims(), _weights(conv_b=FAKE + 8), decode=decode) == E.JM_ERR_ALIGNMENT
+    assert _call(_dims(), x=FAKE + 2, decode=decode) == E.JM_ERR_ALIGNMENT
+    assert _call(_dims(), h_out=None, decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(_dims(), conv_out=None, decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(_dims(), ws=None, decode=decode) == E.JM_ERR_WORKSPACE
+    assert _call(_dims(), ws_bytes=1024, decode=decode) == E.JM_ERR_WORKSPACE
+    assert _call(_dims(), x=None, decode=decode) == E.JM_ERR_INVALID_ARG
+    assert _call(None, decode=decode) == E.JM_ERR_INVALID_ARG
+
+
+def test_decode_requires_input_states_prefill_does_not():
+    assert _call(_dims(), decode=True, conv_in=None) == _lib.JM_ERR_INVALID_ARG
+    assert _call(_dims(), decode=True, h_in=None) == _lib.JM_ERR_INVALID_ARG
+    # prefill with NULL states only fails on the (too small) workspace, i.e. the states were accepted
+    assert _call(_dims(), conv_in=None, h_in=None, ws_bytes=16) == _lib.JM_ERR_WORKSPACE
+
+
+def test_prefill_with_empty_sequence_needs_no_activations():
+    # seqlen 0: x, z, out may be NULL; the call only fails here on the workspace size
+    assert _call(_dims(seqlen=0), x=None, z=None, out=None, ws_bytes=0) == _lib.JM_ERR_WORKSPACE
+    assert _call(_dims(seqlen=-1)) == _lib.JM_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_and_layout():
+    assert jm.prefill_workspace_size(_dims(d_state=8)) == 0
+    assert jm.decode_workspace_size(_dims(d_inner=100)) == 0
+    d = jm.make_dims(1, 4096, 8192, 256, jm.JM_BF16)
+    n = jm.prefill_workspace_size(d)
+    lay = jm.workspace_layout(d)
+    assert lay.total_bytes == n
+    T, C, W = 4096, 8192, 288
+    assert lay.dbc_splits >= 1 and lay.scan_chunks >= 1
+    assert n >= T * C * 2 * 2 + lay.dbc_splits * T * W * 4 + T * 256 * 2 + T * 32 * 4
+    offs = sorted([lay.xc, lay.dbc, lay.dln, lay.bc, lay.delta])
+    assert offs[0] == 0 and all(o % 256 == 0 for o in offs) and offs[-1] < n
+    # decode needs a workspace sized for one token per sequence, independent of seqlen
+    dd = jm.make_dims(256, 9999, 8192, 256, jm.JM_BF16)
+    assert jm.decode_workspace_size(dd) == jm.prefill_workspace_size(jm.make_dims(256, 1, 8192, 256, jm.JM_BF16))
+    with pytest.raises(jm.JMError):
+        jm.workspace_layout(_dims(d_state=4))
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert len(jm.status_string(s)) >= 2
+    assert jm.status_string(-99) == "unknown status"

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by element.
+
+Small cases span several tiles, several scan pieces and ragged tails and are compared in full; the five
+workloads run at full size in the launch configuration the benchmark uses and are compared in full where
+the oracle finishes in seconds (the tiny fp32 mixer, the 4K prefill) and on sampled channels otherwise
+(batched prefill, 256K context, 128 decode steps).  Tolerances are in parity_util.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jm_inputs import CONFIGS, MixerConfig, make_activations, make_decode_tokens, make_state, make_weights, to_f64
+from parity_util import (assert_bitwise, assert_close, log, oracle_long_sampled, oracle_prefill, weights_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mamba_selective_scan_05_amd as jm
+    jm.lib()          # loads the built library or raises
+
+
+def _mixer(cfg: MixerConfig, w):
+    import mamba_selective_scan_05_amd as jm
+    return jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+
+
+def _small(name, B, L, C, R, io, seed, **kw):
+    return MixerConfig(name, batch=B, seqlen=L, d_inner=C, dt_rank=R, io_dtype=io, seed=seed, **kw)
+
+
+def _run_and_check(cfg, with_state=True, row_stride=None, w=None, check_label=""):
+    w = w if w is not None else make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV, row_stride=row_stride)
+    st = make_state(cfg, DEV) if with_state else {"conv_state": None, "ssm_state": None}
+    log(f"[{cfg.name}{check_label}] B={cfg.batch} L={cfg.seqlen} C={cfg.d_inner} R={cfg.dt_rank} {cfg.io_dtype}")
+    m = _mixer(cfg, w)
+    out, cs, hs = m.prefill(a["x"], a["z"], st["conv_state"], st["ssm_state"])
+    torch.cuda.synchronize()
+    w64 = weights_f64(w)
+    h0 = None if st["ssm_state"] is None else to_f64(st["ssm_state"])
+    ro, rc, rh = oracle_prefill(cfg, w64, a["x"], a["z"], st["conv_state"], h0)
+    assert_close("out", out, ro, cfg.io_dtype)
+    assert_close("h_final", hs, rh, cfg.io_dtype)
+    assert_bitwise("conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
+    return m, out, cs, hs
+
+
+# ----------------------------------------------------------------------------- small and ragged cases
+
+def test_tiny_f32_workload():
+    _run_and_check(CONFIGS[0], with_state=False)
+    _run_and_check(CONFIGS[0].replace(with_state=True), with_state=True, check_label="+state")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_ragged_multi_piece(io):
+    # 2 x 700 tokens over 128 channels: the scan runs in several pieces with a ragged last piece, the
+    # projections over several token tiles with a ragged last tile
+    cfg = _small(f"ragged_{io}", 2, 700, 128, 16, io, 11)
+    _run_and_check(cfg)
+
+
+def test_bf16_wide_strided_views():
+    # x and z as strided halves of one [B, L, 2C + 64] buffer, as an in_proj output holds them
+    cfg = _small("bf16_strided", 2, 333, 512, 64, "bf16", 12)
+    _run_and_check(cfg, row_stride=2 * 512 + 64)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 5, 64, 65])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_short_sequences_and_conv_state(L, io):
+    cfg = _small(f"short_L{L}_{io}", 3, L, 64, 8, io, 13)
+    if L == 0:
+        w = make_weights(cfg, DEV)
+        st = make_state(cfg, DEV)
+        m = _mixer(cfg, w)
+        x = torch.empty((3, 0, 64), dtype=cfg.torch_dtype, device=DEV)
+        _, cs, hs = m.prefill(x, x, st["conv_state"], st["ssm_state"])
+        assert_bitwise("conv_state", cs, st["conv_state"])
+        assert torch.equal(hs, st["ssm_state"])
+        return
+    _run_and_check(cfg)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_slow_decay_carries_and_scan_term_alone(io):
+    """A_log - 6 makes the state remember thousands of tokens, so every piece boundary of the scan matters,
+    and D = 0 leaves the scan term alone in the output (no skip term to hide an error)."""
+    cfg = _small(f"slow_decay_{io}", 2, 2500, 128, 16, io, 14)
+    w = make_weights(cfg, DEV)
+    w["A_log"] = (w["A_log"].float() - 6.0).to(cfg.torch_dtype)
+    w["D"] = torch.zeros_like(w["D"])
+    import mamba_selective_scan_05_amd as jm
+    lay = jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen))
+    assert lay.scan_chunks > 1
+    _run_and_check(cfg, w=w)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_intermediates_step_by_step(io):
+    import mamba_selective_scan_05_amd as jm
+    cfg = _small(f"steps_{io}", 2, 300, 256, 64, io, 15)
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    m = _mixer(cfg, w)
+    out, _, _ = m.prefill(a["x"], a["z"])
+    torch.cuda.synchronize()
+    dims = m.dims(cfg.batch, cfg.seqlen)
+    lay = jm.workspace_layout(dims)
+    ws = m._ws
+    T, C, R, W = cfg.batch * cfg.seqlen, cfg.d_inner, cfg.dt_rank, cfg.width
+    dt = cfg.torch_dtype
+    esz = 4 if io == "f32" else 2
+
+    def view(off, n, dtype):
+        nbytes = n * (4 if dtype == torch.float32 else 2)
+        return ws[off:off + nbytes].view(dtype)
+
+    w64 = weights_f64(w)
+    _, _, _, inter = oracle.mixer_prefill(to_f64(a["x"]), to_f64(a["z"]), w64, R, cfg.d_state, cfg.norm_eps,
+                                          return_intermediates=True)
+    xc = view(lay.xc, T * C, dt).view(cfg.batch, cfg.seqlen, C)
+    assert_close("xc", xc, inter["xc"], io)
+    dbc = view(lay.dbc, lay.dbc_splits * T * W, torch.float32).view(lay.dbc_splits, cfg.batch, cfg.seqlen, W).sum(0)
+    assert_close("dbc", dbc, inter["dbc"], io)
+    bc = view(lay.bc, T * 32, torch.float32).view(cfg.batch, cfg.seqlen, 32)
+    assert_close("Bn", bc[..., :16], inter["Bn"], io)
+    assert_close("Cn", bc[..., 16:], inter["Cn"], io)
+    dln = view(lay.dln, T * R, dt).view(cfg.batch, cfg.seqlen, R)
+    assert_close("dln", dln, inter["dln"], io)
+    delta = view(lay.delta, T * C, dt).view(cfg.batch, cfg.seqlen, C)
+    assert_close("delta", delta, inter["delta"], io)
+    del esz
+
+
+@pytest.mark.parametrize("split", [1, 2, 300])
+def test_split_prefill_matches_whole(split):
+    cfg = _small("split", 2, 700, 128, 16, "bf16", 16)
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    st = make_state(cfg, DEV)
+    m = _mixer(cfg, w)
+    x1, z1 = a["x"][:, :split].contiguous(), a["z"][:, :split].contiguous()
+    x2, z2 = a["x"][:, split:].contiguous(), a["z"][:, split:].contiguous()
+    o1, c1, h1 = m.prefill(x1, z1, st["conv_state"], st["ssm_state"])
+    o2, c2, h2 = m.prefill(x2, z2, c1, h1)
+    torch.cuda.synchronize()
+    ro, rc, rh = oracle_prefill(cfg, weights_f64(w), a["x"], a["z"], st["conv_state"], to_f64(st["ssm_state"]))
+    assert_close("out", torch.cat([o1, o2], dim=1), ro, "bf16")
+    assert_close("h_final", h2, rh, "bf16")
+    assert_bitwise("conv_state", c2, torch.from_numpy(rc).to(cfg.torch_dtype))
+
+
+@pytest.mark.parametrize("L", [2, 700])
+def test_states_updated_in_place(L):
+    cfg = _small("inplace", 2, L, 128, 16, "bf16", 17)
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    st = make_state(cfg, DEV)
+    ro, rc, rh = oracle_prefill(cfg, weights_f64(w), a["x"], a["z"], st["conv_state"], to_f64(st["ssm_state"]))
+    m = _mixer(cfg, w)
+    cs, hs = st["conv_state"].clone(), st["ssm_state"].clone()
+    out, cs2, hs2 = m.prefill(a["x"], a["z"], cs, hs, conv_state_out=cs, ssm_state_out=hs)
+    torch.cuda.synchronize()
+    assert cs2.data_ptr() == cs.data_ptr() and hs2.data_ptr() == hs.data_ptr()
+    assert_close("out", out, ro, "bf16")
+    assert_close("h_final", hs, rh, "bf16")
+    assert_bitwise("conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_steps_small(io):
+    cfg = _small(f"decode_{io}", 3, 1, 128, 16, io, 18, decode_steps=6, with_state=True)
+    w = make_weights(cfg, DEV)
+    st = make_state(cfg, DEV)
+    tok = make_decode_tokens(cfg, DEV)
+    m = _mixer(cfg, w)
+    cs, hs = st["conv_state"].clone(), st["ssm_state"].clone()
+    outs = []
+    for t in range(cfg.decode_steps):
+        o, _, _ = m.decode_step(tok["x"][:, t], tok["z"][:, t], cs, hs, in_place=True)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    ro, rc, rh = oracle_prefill(cfg, weights_f64(w), tok["x"], tok["z"], st["conv_state"], to_f64(st["ssm_state"]))
+    assert_close("decode out", torch.stack(outs, dim=1), ro, io)
+    assert_close("h_final", hs, rh, io)
+    assert_bitwise("conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
+
+
+def test_deterministic_and_every_output_written():
+    cfg = _small("determinism", 2, 700, 256, 64, "bf16", 19)
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    m = _mixer(cfg, w)
+    nan = torch.full((2, 700, 256), float("nan"), dtype=cfg.torch_dtype, device=DEV)
+    o1, c1, h1 = m.prefill(a["x"], a["z"], out=nan.clone(),
+                           conv_state_out=torch.full((2, 256, 3), float("nan"), dtype=cfg.torch_dtype, device=DEV),
+                           ssm_state_out=torch.full((2, 256, 16), float("nan"), device=DEV))
+    m._ws.fill_(0xFF)   # poison the workspace between the runs: nothing may depend on its old contents
+    o2, c2, h2 = m.prefill(a["x"], a["z"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(h1).all() and torch.isfinite(c1.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(c1, c2)
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+def test_workload_prefill_4k_full():
+    cfg = CONFIGS[1]
+    _run_and_check(cfg, with_state=False)
+
+
+def test_workload_batched_prefill_sampled_channels():
+    cfg = CONFIGS[2]
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    log(f"[{cfg.name}] B={cfg.batch} L={cfg.seqlen} C={cfg.d_inner}")
+    m = _mixer(cfg, w)
+    out, cs, hs = m.prefill(a["x"], a["z"])
+    torch.cuda.synchronize()
+    sel = np.arange(3, cfg.d_inner, 61)          # 135 channels spread over all 64-channel groups
+    ro, rc, rh = oracle_prefill(cfg, weights_f64(w), a["x"], a["z"], channels=sel)
+    assert_close("out[sampled]", out[..., torch.as_tensor(sel, device=DEV)], ro, "bf16")
+    assert_close("h_final[sampled]", hs[:, torch.as_tensor(sel, device=DEV)], rh, "bf16")
+    assert_bitwise("conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
+
+
+def test_workload_long_context_256k_sampled_channels():
+    cfg = CONFIGS[3]
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    log(f"[{cfg.name}] B={cfg.batch} L={cfg.seqlen} C={cfg.d_inner}")
+    m = _mixer(cfg, w)
+    out, cs, hs = m.prefill(a["x"], a["z"])
+    torch.cuda.synchronize()
+    sel = np.array([0, 77, 1000, 2049, 4095, 5120, 6143, 8191])
+    sel_t = torch.as_tensor(sel, device=DEV)
+    log("  oracle on sampled channels ...")
+    ro, rh, rc = oracle_long_sampled(cfg, weights_f64(w), a["x"], a["z"], sel)
+    assert_close("out[sampled]", out.index_select(2, sel_t), ro, "bf16")
+    assert_close("h_final[sampled]", hs.index_select(1, sel_t), rh, "bf16")
+    assert_bitwise("conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
+
+
+def test_workload_decode_128_steps():
+    cfg = CONFIGS[4]
+    w = make_weights(cfg, DEV)
+    st = make_state(cfg, DEV)
+    tok = make_decode_tokens(cfg, DEV)
+    log(f"[{cfg.name}] B={cfg.batch} steps={cfg.decode_steps} C={cfg.d_inner}")
+    m = _mixer(cfg, w)
+    cs, hs = st["conv_state"].clone(), st["ssm_state"].clone()
+    outs = torch.empty((cfg.batch, cfg.decode_steps, cfg.d_inner), dtype=cfg.torch_dtype, device=DEV)
+    for t in range(cfg.decode_steps):
+        o, _, _ = m.decode_step(tok["x"][:, t], tok["z"][:, t], cs, hs, in_place=True)
+        outs[:, t] = o
+    # the same 128 tokens as one prefill from the same states
+    po, pc, ph = m.prefill(tok["x"], tok["z"], st["conv_state"], st["ssm_state"])
+    torch.cuda.synchronize()
+    sel = np.arange(5, cfg.d_inner, 67)
+    sel_t = torch.as_tensor(sel, device=DEV)
+    ro, rc, rh = oracle_prefill(cfg, weights_f64(w), tok["x"], tok["z"], st["conv_state"],
+                                to_f64(st["ssm_state"])[:, sel], channels=sel)
+    assert_close("decode out[sampled]", outs.index_select(2, sel_t), ro, "bf16")
+    assert_close("decode h_final[sampled]", hs.index_select(1, sel_t), rh, "bf16")
+    assert_bitwise("decode conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
+    assert_close("prefill out[sampled]", po.index_select(2, sel_t), ro, "bf16")
+    # GPU decode against GPU prefill over every channel
+    assert_close("decode vs prefill out", outs, po.double().cpu().numpy(), "bf16")
+    assert_close("decode vs prefill h", hs, ph.double().cpu().numpy(), "bf16")
+    assert_bitwise("decode vs prefill conv", cs, pc)
