@@ -145,6 +145,8 @@ def _row_stride(t: torch.Tensor, rows_per_batch: int) -> int:
     if t.stride(-1) != 1:
         raise ValueError("the channel dimension must be contiguous")
     rs = t.stride(-2) if t.dim() == 3 else t.stride(0)
+    if t.numel() == 0:
+        return int(t.shape[-1])
     if t.dim() == 3 and t.shape[0] > 1 and t.stride(0) != rows_per_batch * rs:
         raise ValueError("rows must be evenly spaced across the batch")
     return int(rs)

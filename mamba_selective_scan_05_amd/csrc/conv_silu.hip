@@ -31,6 +31,16 @@ __device__ __forceinline__ void load16(const T* p, float* out) {
 }
 
 template <typename T>
+__device__ __forceinline__ void unpack16(uint4 raw, float* out) {
+  Vec16<T> r;
+  memcpy(&r, &raw, 16);
+#pragma unroll
+  for (int i = 0; i < Vec16<T>::n; ++i) out[i] = io<T>::cvt(r.v[i]);
+}
+
+constexpr int kRows = 8;   // rows per prefetch batch
+
+template <typename T>
 __device__ __forceinline__ void store16(T* p, const float* in) {
   Vec16<T> r;
 #pragma unroll
@@ -82,23 +92,45 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T* __restrict__ x,
     for (int j = 0; j < kTaps - 1; ++j) load16(x + ((int64_t)b * L + t0 - (kTaps - 1) + j) * xs + c0, prev[j]);
   }
 
-  for (int t = t0; t < t1; ++t) {
-    const int64_t row = (int64_t)b * L + t;
-    float cur[V], o[V];
-    load16(x + row * xs + c0, cur);
+  // Rows arrive in batches of kRows; the next batch's 16-byte loads are in flight while the current one is
+  // computed (two register buffers used in turn).  Prefetch rows are clamped to the run, so they stay in
+  // bounds without branches.
+  const T* xb = x + (int64_t)b * L * xs + c0;
+  T* ob = xc + (int64_t)b * L * C + c0;
+  auto load_rows = [&](int tb, uint4* buf) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      float u = bias[i];
-      u = fmaf(w[i][0], prev[0][i], u);
-      u = fmaf(w[i][1], prev[1][i], u);
-      u = fmaf(w[i][2], prev[2][i], u);
-      u = fmaf(w[i][3], cur[i], u);
-      o[i] = silu(u);
-      prev[0][i] = prev[1][i];
-      prev[1][i] = prev[2][i];
-      prev[2][i] = cur[i];
+    for (int j = 0; j < kRows; ++j) buf[j] = *reinterpret_cast<const uint4*>(xb + (int64_t)min(tb + j, t1 - 1) * xs);
+  };
+  auto conv_rows = [&](int tb, const uint4* buf) {
+    const int count = min(kRows, t1 - tb);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      if (j >= count) break;
+      float cur[V], o[V];
+      unpack16<T>(buf[j], cur);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float u = bias[i];
+        u = fmaf(w[i][0], prev[0][i], u);
+        u = fmaf(w[i][1], prev[1][i], u);
+        u = fmaf(w[i][2], prev[2][i], u);
+        u = fmaf(w[i][3], cur[i], u);
+        o[i] = silu(u);
+        prev[0][i] = prev[1][i];
+        prev[1][i] = prev[2][i];
+        prev[2][i] = cur[i];
+      }
+      store16(ob + (int64_t)(tb + j) * C, o);
     }
-    store16(xc + row * C + c0, o);
+  };
+  uint4 bufA[kRows], bufB[kRows];
+  load_rows(t0, bufA);
+  for (int tb = t0; tb < t1; tb += 2 * kRows) {
+    if (tb + kRows < t1) load_rows(tb + kRows, bufB);
+    conv_rows(tb, bufA);
+    if (tb + kRows >= t1) break;
+    if (tb + 2 * kRows < t1) load_rows(tb + 2 * kRows, bufA);
+    conv_rows(tb + kRows, bufB);
   }
 }
 
@@ -122,7 +154,7 @@ __global__ void state_passthrough_kernel(const T* __restrict__ conv_in, T* __res
 void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
                       const void* conv_in, void* xc, int B, int L, int C, hipStream_t st) {
   const int V = bf16 ? 8 : 4;
-  const int run = L >= 4096 ? 64 : 32;
+  const int run = 32;
   dim3 block(256);
   dim3 grid((C / V + 255) / 256, (L + run - 1) / run, B);
   if (bf16)

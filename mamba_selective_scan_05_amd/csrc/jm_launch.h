@@ -10,6 +10,11 @@ namespace jm {
 void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
                       const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
 
+// Tokens per x_proj workgroup tile (bf16 path).
+int xproj_token_tile();
+// Most channel slices the x_proj contraction may be split over (the norm step adds at most this many).
+constexpr int kMaxXprojSplits = 16;
+
 // dbc partial sums: part[s, m, n] = sum over channel slice s of xc[m, k] * w[n, k].
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
                   hipStream_t st);

@@ -14,10 +14,10 @@ constexpr int kMaxR = 512;   // dt_rank bound of the norm kernel
 constexpr int64_t kAlign = 256;
 
 // Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.
-constexpr int64_t kScanWaveTarget = 2048;
-constexpr int kMinPiece = 256;
-// x_proj: aim for at least this many workgroups before splitting the contraction over channel slices.
-constexpr int kXprojWgTarget = 512;
+constexpr int64_t kScanWaveTarget = 4096;
+constexpr int kMinPiece = 128;
+// x_proj: split the contraction over channel slices until there are this many workgroups (one per CU).
+constexpr int kXprojWgTarget = 256;
 
 struct Plan {
   int B, L, C, N, R, W;
@@ -65,8 +65,11 @@ Plan make_plan(const jm_mixer_dims* d, bool decode) {
   // x_proj split: channel slices of a multiple of 64, dividing C, until the grid is big enough.
   p.splits = 1;
   if (p.bf16) {
-    const int64_t mtiles = (p.T + 63) / 64;
-    while (mtiles * p.splits < kXprojWgTarget && (p.C / 64) % (p.splits * 2) == 0) p.splits *= 2;
+    const int64_t tile = jm::xproj_token_tile();
+    const int64_t mtiles = (p.T + tile - 1) / tile;
+    while (mtiles * p.splits < kXprojWgTarget && p.splits * 2 <= jm::kMaxXprojSplits &&
+           (p.C / 64) % (p.splits * 2) == 0)
+      p.splits *= 2;
   }
 
   // scan pieces
@@ -164,7 +167,6 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
                   dims->norm_eps, dln, bc, st);
   marks.mark(3);
   jm::launch_dtproj(p.bf16, dln, w->dt_proj_w, w->dt_proj_b, delta, (int)p.T, p.C, p.R, st);
-  marks.mark(4);
   jm::ScanArgs a;
   a.xc = xc;
   a.delta = delta;
@@ -187,7 +189,8 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.C = p.C;
   a.P = p.P;
   a.Lp = p.Lp;
-  jm::launch_scan(p.bf16, a, st, events ? &marks.ev[5] : nullptr);
+  // the scan records events[4] (local pass), events[5] (carry pass) and events[6] (full pass)
+  jm::launch_scan(p.bf16, a, st, events ? &marks.ev[4] : nullptr);
   marks.mark(JM_STAGES);
   return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
 }

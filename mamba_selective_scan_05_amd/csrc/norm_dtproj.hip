@@ -1,13 +1,17 @@
 // Jamba's RMSNorms on the selective parameters, then dt_proj + bias + softplus.
 //
-// norm: one wave per token adds the x_proj partial sums in slice order, then RMSNorms the dt slice (R
-// values), the B slice and the C slice (N values each) separately: v / sqrt(mean(v^2) + eps) * w.  The
-// normalised dt goes out in the I/O dtype (it is the next contraction's operand), B and C in fp32.
+// norm: one wave per token adds the x_proj partial sums in slice order (all slices of a column are loaded
+// together, then added in order, so the result does not depend on timing), then RMSNorms the dt slice
+// (R values), the B slice and the C slice (N values each) separately: v / sqrt(mean(v^2) + eps) * w.
+// The normalised dt goes out in the I/O dtype (it is the next contraction's operand), B and C in fp32.
 //
 // dt_proj: delta[m, c] = softplus(sum_r dln[m, r] * W[c, r] + b[c]).  bf16 path on matrix cores
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation): a workgroup of 4 waves computes a 64-token x 256-channel
-// tile, each wave 64 x 64, with the bias and softplus fused into the epilogue.  fp32 path on the vector
-// ALU.
+// tile, each wave 64 x 64.  The dln tile is staged once in LDS for the 4 waves; each wave issues all its
+// W_dt fragment loads up front.  Bias and softplus are fused into the epilogue, which transposes the tile
+// through LDS so that delta rows leave in 16-byte stores.  Workgroups are mapped so that each XCD walks
+// the token tiles of a fixed set of channel blocks, keeping those W_dt rows in its L2.  fp32 path on the
+// vector ALU.
 #include "jm_device.h"
 #include "jm_launch.h"
 
@@ -29,14 +33,21 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
   const int m = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (m >= M) return;
   const int W = R + 2 * N;
+  const int64_t slice = (int64_t)M * W;
+  const float* src = part + (int64_t)m * W;
   float v[kMaxCols];
   float ss_dt = 0.f, ss_b = 0.f, ss_c = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxCols; ++i) {
     const int col = lane + 64 * i;
     float s = 0.f;
-    if (col < W)
-      for (int p = 0; p < splits; ++p) s += part[((int64_t)p * M + m) * W + col];
+    if (col < W) {
+      float pv[kMaxXprojSplits];
+#pragma unroll
+      for (int p = 0; p < kMaxXprojSplits; ++p) pv[p] = p < splits ? src[p * slice + col] : 0.0f;
+#pragma unroll
+      for (int p = 0; p < kMaxXprojSplits; ++p) s += pv[p];
+    }
     v[i] = s;
     const float sq = s * s;
     if (col < R) ss_dt += sq;
@@ -62,52 +73,121 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
   }
 }
 
-__device__ __forceinline__ bf16x8 ld_bf16x8_guard(const bf16_t* p, bool ok) {
+constexpr int kDtMaxR = 256;            // dt_rank of the staged bf16 path (larger ranks loop in slices)
+constexpr int kDtLd = kDtMaxR + 8;      // padded LDS row of the dln tile
+constexpr int kDtOutLd = 64 + 8;        // padded LDS row of a wave's output tile (bf16)
+
+__device__ __forceinline__ bf16x8 ld16_guard(const bf16_t* p, bool ok) {
   uint4 raw = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
   return __builtin_bit_cast(bf16x8, raw);
 }
 
-// 64 tokens x 256 channels per workgroup; wave w owns channels [64w, 64w + 64) of the tile.
-__global__ __launch_bounds__(256) void dtproj_mfma_kernel(const bf16_t* __restrict__ dln,
-                                                          const bf16_t* __restrict__ w,
-                                                          const bf16_t* __restrict__ bias,
-                                                          bf16_t* __restrict__ delta, int M, int C, int R) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// 64 tokens x 256 channels per workgroup; wave w owns channels [64w, 64w + 64) of the tile.  The LDS of
+// the dln tile is reused for the output transpose once the products are done.
+constexpr int kDtLdsBytes = (64 * kDtLd * 2 > 4 * 64 * kDtOutLd * 2) ? 64 * kDtLd * 2 : 4 * 64 * kDtOutLd * 2;
+__global__ __launch_bounds__(256, 2) void dtproj_mfma_kernel(const bf16_t* __restrict__ dln,
+                                                             const bf16_t* __restrict__ w,
+                                                             const bf16_t* __restrict__ bias,
+                                                             bf16_t* __restrict__ delta, int M, int C, int R) {
+  __shared__ __attribute__((aligned(16))) char lds[kDtLdsBytes];
+  bf16_t* As = reinterpret_cast<bf16_t*>(lds);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const int c0 = blockIdx.x * 256 + wave * 64;
-  const int m0 = blockIdx.y * 64;
+  // XCD-aware order: workgroup i runs on XCD i % 8; XCD x takes channel blocks x, x + 8, ... and walks
+  // all token tiles of one channel block before the next.
+  const int ncb = (C + 255) / 256, nmt = (M + 63) / 64;
+  const int i = blockIdx.x;
+  int cb, mt;
+  if (ncb % 8 == 0) {
+    const int x = i % 8, j = i / 8;
+    cb = x + 8 * (j / nmt);
+    mt = j % nmt;
+  } else {
+    cb = i / nmt;
+    mt = i % nmt;
+  }
+  const int c0 = cb * 256 + wave * 64;
+  const int m0 = mt * 64;
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (c0 >= C) return;
-  for (int k = 0; k < R; k += 32) {
-    const bool kok = k + lk < R;   // R % 8 == 0: an 8-wide k group is wholly in or out
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + r * 16 + lr;
-      a[r] = ld_bf16x8_guard(dln + (int64_t)m * R + k + lk, kok && m < M);
+
+  for (int kr = 0; kr < R; kr += kDtMaxR) {
+    const int rk = min(kDtMaxR, R - kr);
+    __syncthreads();
+    // stage the dln tile [64 x rk] (rk % 8 == 0)
+    for (int q = tid; q < 64 * (kDtMaxR / 8); q += 256) {
+      const int row = q / (kDtMaxR / 8), kc = (q % (kDtMaxR / 8)) * 8;
+      const int m = m0 + row;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m < M && kc < rk) v = *reinterpret_cast<const uint4*>(dln + (int64_t)m * R + kr + kc);
+      *reinterpret_cast<uint4*>(&As[row * kDtLd + kc]) = v;
     }
+    __syncthreads();
+    if (c0 < C) {
+      // W_dt fragments two k-steps at a time: the next pair is in flight while the current pair multiplies
+      auto ldb = [&](int ks, bf16x8* b) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b[t] = ld_bf16x8_guard(w + (int64_t)(c0 + t * 16 + lr) * R + k + lk, kok);
+        for (int t = 0; t < 4; ++t)
+          b[t] = ld16_guard(w + (int64_t)(c0 + t * 16 + lr) * R + kr + ks * 32 + lk, ks * 32 + lk < rk);
+      };
+      bf16x8 b0[4], b1[4], n0[4], n1[4];
+      ldb(0, b0);
+      ldb(1, b1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int ks = 0; ks < kDtMaxR / 32; ks += 2) {
+        if (ks + 2 < kDtMaxR / 32) {
+          ldb(ks + 2, n0);
+          ldb(ks + 3, n1);
+        }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b[t], acc[r][t], 0, 0, 0);
-  }
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 a[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int c = c0 + t * 16 + lr;
-    const float bc_ = bf2f(bias[c]);
+          for (int r = 0; r < 4; ++r)
+            a[r] = *reinterpret_cast<const bf16x8*>(&As[(r * 16 + lr) * kDtLd + (ks + h) * 32 + lk]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + r * 16 + (lane >> 4) * 4 + i;
-        if (m < M) delta[(int64_t)m * C + c] = f2bf(softplus(acc[r][t][i] + bc_));
+            for (int t = 0; t < 4; ++t)
+              acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], h ? b1[t] : b0[t], acc[r][t], 0, 0, 0);
+        }
+        if (ks + 2 < kDtMaxR / 32) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            b0[t] = n0[t];
+            b1[t] = n1[t];
+          }
+        }
       }
+    }
+  }
+  // epilogue: bias + softplus, bf16, through LDS so that each lane stores 16 contiguous bytes.  Waves past
+  // the last channel block only take part in the barriers.
+  const bool active = c0 < C;
+  __syncthreads();   // every wave is done reading the dln tile: its LDS now holds the output tiles
+  bf16_t* os = reinterpret_cast<bf16_t*>(lds) + wave * 64 * kDtOutLd;
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float bc_ = bf2f(bias[c0 + t * 16 + lr]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+          os[(r * 16 + (lane >> 4) * 4 + i2) * kDtOutLd + t * 16 + lr] = f2bf(softplus(acc[r][t][i2] + bc_));
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int id = lane + 64 * q, row = id >> 3, cc = (id & 7) * 8;
+    const int m = m0 + row;
+    if (m < M) *reinterpret_cast<uint4*>(delta + (int64_t)m * C + c0 + cc) = *reinterpret_cast<const uint4*>(&os[row * kDtOutLd + cc]);
   }
 }
 
@@ -140,8 +220,8 @@ void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, voi
                    hipStream_t st) {
   if (M == 0) return;
   if (bf16) {
-    dim3 grid((C + 255) / 256, (M + 63) / 64);
-    hipLaunchKernelGGL(dtproj_mfma_kernel, grid, dim3(256), 0, st, (const bf16_t*)dln, (const bf16_t*)w,
+    const int ncb = (C + 255) / 256, nmt = (M + 63) / 64;
+    hipLaunchKernelGGL(dtproj_mfma_kernel, dim3(ncb * nmt), dim3(256), 0, st, (const bf16_t*)dln, (const bf16_t*)w,
                        (const bf16_t*)b, (bf16_t*)delta, M, C, R);
   } else {
     dim3 grid((C + 255) / 256, M);

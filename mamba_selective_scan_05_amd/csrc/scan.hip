@@ -6,7 +6,10 @@
 //
 // One lane owns one channel of one sequence and keeps its 16-wide fp32 state in registers; B_t and C_t
 // are shared by every channel, so a wave reads them as wave-uniform (scalar) loads.  exp(delta * A) is
-// evaluated as 2^(delta * A * log2 e) with A * log2 e precomputed per state.
+// evaluated as 2^(delta * A * log2 e) with A * log2 e precomputed per state.  Tokens are processed in
+// batches of 8 whose per-channel loads (delta, xc, z) are issued one batch ahead, so HBM latency hides
+// behind the arithmetic of the current batch.  The kernel is bound by the vector ALU (16 exponentials
+// and about 64 other operations per token and channel), not by HBM.
 //
 // Two levels, so that short batches still fill the GPU: each sequence is cut into P pieces of Lp tokens.
 //   local  : every piece but the last runs the recurrence from a zero state (piece 0 from the initial
@@ -25,40 +28,206 @@ namespace {
 
 constexpr int kN = 16;
 constexpr int kTaps = 4;
+constexpr int kBatch = 8;   // tokens per prefetch batch
 
+// Buffer resource over [base, base + bytes): raw (untyped) accesses, 32-bit byte offsets.
+constexpr int kBufferFlags = 0x00020000;   // dword 3 of a raw buffer descriptor on gfx9-family GPUs
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferFlags);
+}
+
+// A raw element held in a full 32-bit register: bf16 zero-extended (widened with a shift when used),
+// fp32 as is.  Loads and stores go through a buffer resource with a per-lane byte offset (the channel)
+// and a wave-uniform byte offset (the token row), so no per-access vector address arithmetic is needed.
+template <typename T> struct Raw;
+template <> struct Raw<bf16_t> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ uint32_t ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ float f(uint32_t v) { return __uint_as_float(v << 16); }
+};
+template <> struct Raw<float> {
+  typedef float type;
+  // the b32 buffer builtins move 32-bit integers: reinterpret, never convert
+  static __device__ __forceinline__ float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ float f(float v) { return v; }
+};
+
+// a2[n] = A[c, n] * log2(e) = -exp(A_log[c, n]) * log2(e), with the hardware exp (about 1 ulp)
 template <typename T>
 __device__ __forceinline__ void load_a2(const T* A_log, int c, float* a2) {
 #pragma unroll
-  for (int n = 0; n < kN; ++n) a2[n] = -expf(io<T>::ld(A_log + (int64_t)c * kN + n)) * kLog2e;
+  for (int n = 0; n < kN; ++n) a2[n] = -exp2_fast(io<T>::ld(A_log + (int64_t)c * kN + n) * kLog2e) * kLog2e;
 }
 
-template <typename T>
-__global__ __launch_bounds__(64) void scan_local_kernel(const T* __restrict__ xc, const T* __restrict__ delta,
-                                                        const float* __restrict__ bc, const T* __restrict__ A_log,
-                                                        const float* __restrict__ h0, float* __restrict__ loc,
-                                                        int L, int C, int P, int Lp) {
+// FULL = false: the local pass (end state + delta sum of a piece); FULL = true: the output pass.
+template <typename T, bool FULL>
+__global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   const int c = blockIdx.x * 64 + threadIdx.x;
   const int p = blockIdx.y;
   const int b = blockIdx.z;
+  const int L = a.L, C = a.C, P = a.P;
+  const int t0 = p * a.Lp, t1 = min(L, t0 + a.Lp);
+
   float a2[kN], h[kN];
-  load_a2(A_log, c, a2);
+  load_a2((const T*)a.A_log, c, a2);
+  if (FULL && P > 1) {
+    const float* src = a.cin + ((int64_t)b * P + p) * kN * C + c;
 #pragma unroll
-  for (int n = 0; n < kN; ++n) h[n] = (p == 0 && h0) ? h0[((int64_t)b * C + c) * kN + n] : 0.0f;
-  float sdt = 0.f;
-  const int t0 = p * Lp, t1 = min(L, t0 + Lp);
-  for (int t = t0; t < t1; ++t) {
-    const int64_t row = (int64_t)b * L + t;
-    const float dt = io<T>::ld(delta + row * C + c);
-    const float u = dt * io<T>::ld(xc + row * C + c);
-    const float* Bt = bc + row * (2 * kN);
+    for (int n = 0; n < kN; ++n) h[n] = src[(int64_t)n * C];
+  } else if (p == 0 && a.h0) {
+    const float* src = a.h0 + ((int64_t)b * C + c) * kN;
 #pragma unroll
-    for (int n = 0; n < kN; ++n) h[n] = fmaf(exp2_fast(dt * a2[n]), h[n], u * Bt[n]);
-    sdt += dt;
+    for (int n = 0; n < kN; ++n) h[n] = src[n];
+  } else {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) h[n] = 0.0f;
   }
-  float* dst = loc + ((int64_t)b * P + p) * (kN + 1) * C + c;
+  const float Dc = FULL ? io<T>::ld((const T*)a.D + c) : 0.0f;
+
+  // Per-piece buffer resources (the plan keeps a piece under 2 GiB), a per-lane channel offset and a
+  // wave-uniform token offset.
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int n_tok = t1 - t0;
+  const int64_t zs = a.z_stride;
+  const int64_t rows = n_tok > 0 ? n_tok : 1;
+  const __amdgpu_buffer_rsrc_t dres = make_rsrc((const T*)a.delta + row0 * C, rows * C * (int64_t)sizeof(T));
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc((const T*)a.xc + row0 * C, rows * C * (int64_t)sizeof(T));
+  const __amdgpu_buffer_rsrc_t zres = make_rsrc((const T*)a.z + row0 * zs, rows * zs * (int64_t)sizeof(T));
+  const __amdgpu_buffer_rsrc_t ores = make_rsrc((T*)a.out + row0 * C, rows * C * (int64_t)sizeof(T));
+  const uint32_t voff = (uint32_t)c * sizeof(T);
+  const uint32_t row_bytes = (uint32_t)(C * sizeof(T)), zrow_bytes = (uint32_t)(zs * sizeof(T));
+  // B and C were written by an earlier kernel and are read-only here: reading them through the constant
+  // address space lets every wave fetch them with scalar loads.
+  const __attribute__((address_space(4))) float* bcp =
+      (const __attribute__((address_space(4))) float*)(a.bc + row0 * (2 * kN));
+
+  // Raw per-channel inputs are held as 32-bit words (zero-extended for bf16) so that a load in flight
+  // never has to be merged into a half register before it is needed.  Prefetch indices are clamped to the
+  // piece, so loads past its end re-read its last token instead of branching.
+  typedef typename Raw<T>::type R;
+  auto load_batch = [&](int i0, R* d, R* x, R* z) {
 #pragma unroll
-  for (int n = 0; n < kN; ++n) dst[(int64_t)n * C] = h[n];
-  dst[(int64_t)kN * C] = sdt;
+    for (int j = 0; j < kBatch; ++j) {
+      const uint32_t i = (uint32_t)min(i0 + j, n_tok - 1);
+      d[j] = Raw<T>::ld(dres, voff, i * row_bytes);
+      x[j] = Raw<T>::ld(xres, voff, i * row_bytes);
+      if (FULL) z[j] = Raw<T>::ld(zres, voff, i * zrow_bytes);
+    }
+  };
+  float sdt = 0.0f;
+  // one token: B_t / C_t come in as wave-uniform values
+  auto step = [&](int i, R draw, R xraw, R zraw, const float* Bt, const float* Ct) {
+    const float dt = Raw<T>::f(draw);
+    const float xv = Raw<T>::f(xraw);
+    const float u = dt * xv;
+    if (FULL) {
+      float y = 0.0f;
+#pragma unroll
+      for (int n = 0; n < kN; ++n) {
+        h[n] = fmaf(exp2_fast(dt * a2[n]), h[n], u * Bt[n]);
+        y = fmaf(Ct[n], h[n], y);
+      }
+      y = fmaf(Dc, xv, y);
+      Raw<T>::st(ores, voff, (uint32_t)i * row_bytes, y * silu(Raw<T>::f(zraw)));
+    } else {
+#pragma unroll
+      for (int n = 0; n < kN; ++n) h[n] = fmaf(exp2_fast(dt * a2[n]), h[n], u * Bt[n]);
+      sdt += dt;
+    }
+  };
+  // a batch of kBatch tokens starting at i0 whose inputs are in d/x/z; count < kBatch only for the last
+  auto run_batch = [&](int i0, const R* d, const R* x, const R* z) {
+    const int count = min(kBatch, n_tok - i0);
+    if (count == kBatch) {
+      float Bc[kN], Cc[kN];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) {
+        Bc[n] = bcp[(int64_t)i0 * (2 * kN) + n];
+        Cc[n] = FULL ? bcp[(int64_t)i0 * (2 * kN) + kN + n] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        // B / C of the next token are requested before this token's arithmetic
+        float Bn[kN], Cn[kN];
+        if (j + 1 < kBatch) {
+#pragma unroll
+          for (int n = 0; n < kN; ++n) {
+            Bn[n] = bcp[(int64_t)(i0 + j + 1) * (2 * kN) + n];
+            Cn[n] = FULL ? bcp[(int64_t)(i0 + j + 1) * (2 * kN) + kN + n] : 0.0f;
+          }
+        }
+        step(i0 + j, d[j], x[j], z[j], Bc, Cc);
+        if (j + 1 < kBatch) {
+#pragma unroll
+          for (int n = 0; n < kN; ++n) {
+            Bc[n] = Bn[n];
+            Cc[n] = Cn[n];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (j >= count) break;
+        float Bt[kN], Ct[kN];
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+          Bt[n] = bcp[(int64_t)(i0 + j) * (2 * kN) + n];
+          Ct[n] = FULL ? bcp[(int64_t)(i0 + j) * (2 * kN) + kN + n] : 0.0f;
+        }
+        step(i0 + j, d[j], x[j], z[j], Bt, Ct);
+      }
+    }
+  };
+
+  // ping-pong buffers: batch k computes from one set while batch k+1 loads into the other
+  R dA[kBatch], xA[kBatch], zA[kBatch], dB[kBatch], xB[kBatch], zB[kBatch];
+  if (n_tok > 0) load_batch(0, dA, xA, zA);
+  for (int i0 = 0; i0 < n_tok; i0 += 2 * kBatch) {
+    if (i0 + kBatch < n_tok) load_batch(i0 + kBatch, dB, xB, zB);
+    run_batch(i0, dA, xA, zA);
+    if (i0 + kBatch >= n_tok) break;
+    if (i0 + 2 * kBatch < n_tok) load_batch(i0 + 2 * kBatch, dA, xA, zA);
+    run_batch(i0 + kBatch, dB, xB, zB);
+  }
+
+  if (!FULL) {
+    float* dst = a.loc + ((int64_t)b * P + p) * (kN + 1) * C + c;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) dst[(int64_t)n * C] = h[n];
+    dst[(int64_t)kN * C] = sdt;
+    return;
+  }
+  if (p == P - 1) {
+    float* ho = a.h_out + ((int64_t)b * C + c) * kN;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) ho[n] = h[n];
+    // conv state: the last K-1 entries of the extended input (old state entries when L < K-1).  All three
+    // are read before any is written, so conv_out may alias conv_in.
+    const T* x = (const T*)a.x;
+    const T* ci = (const T*)a.conv_in;
+    T v[kTaps - 1];
+#pragma unroll
+    for (int j = 0; j < kTaps - 1; ++j) {
+      const int tau = L - (kTaps - 1) + j;
+      if (tau >= 0) v[j] = x[((int64_t)b * L + tau) * a.x_stride + c];
+      else v[j] = ci ? ci[((int64_t)b * C + c) * (kTaps - 1) + tau + (kTaps - 1)] : io<T>::from(0.0f);
+    }
+    T* co = (T*)a.conv_out + ((int64_t)b * C + c) * (kTaps - 1);
+#pragma unroll
+    for (int j = 0; j < kTaps - 1; ++j) co[j] = v[j];
+  }
 }
 
 template <typename T>
@@ -85,66 +254,6 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) void scan_full_kernel(ScanArgs a) {
-  const int c = blockIdx.x * 64 + threadIdx.x;
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
-  const int L = a.L, C = a.C;
-  const T* xc = (const T*)a.xc;
-  const T* delta = (const T*)a.delta;
-  const T* z = (const T*)a.z;
-  T* out = (T*)a.out;
-  float a2[kN], h[kN];
-  load_a2((const T*)a.A_log, c, a2);
-  const float Dc = io<T>::ld((const T*)a.D + c);
-  if (a.P == 1) {
-#pragma unroll
-    for (int n = 0; n < kN; ++n) h[n] = a.h0 ? a.h0[((int64_t)b * C + c) * kN + n] : 0.0f;
-  } else {
-    const float* src = a.cin + ((int64_t)b * a.P + p) * kN * C + c;
-#pragma unroll
-    for (int n = 0; n < kN; ++n) h[n] = src[(int64_t)n * C];
-  }
-  const int t0 = p * a.Lp, t1 = min(L, t0 + a.Lp);
-  for (int t = t0; t < t1; ++t) {
-    const int64_t row = (int64_t)b * L + t;
-    const float dt = io<T>::ld(delta + row * C + c);
-    const float xv = io<T>::ld(xc + row * C + c);
-    const float zv = io<T>::ld(z + row * a.z_stride + c);
-    const float u = dt * xv;
-    const float* Bt = a.bc + row * (2 * kN);
-    const float* Ct = Bt + kN;
-    float y = 0.f;
-#pragma unroll
-    for (int n = 0; n < kN; ++n) {
-      h[n] = fmaf(exp2_fast(dt * a2[n]), h[n], u * Bt[n]);
-      y = fmaf(Ct[n], h[n], y);
-    }
-    y = fmaf(Dc, xv, y);
-    io<T>::st(out + row * C + c, y * silu(zv));
-  }
-  if (p == a.P - 1) {
-    float* ho = a.h_out + ((int64_t)b * C + c) * kN;
-#pragma unroll
-    for (int n = 0; n < kN; ++n) ho[n] = h[n];
-    // conv state: the last K-1 entries of the extended input (old state entries when L < K-1).  All three
-    // are read before any is written, so conv_out may alias conv_in.
-    const T* x = (const T*)a.x;
-    const T* ci = (const T*)a.conv_in;
-    T v[kTaps - 1];
-#pragma unroll
-    for (int j = 0; j < kTaps - 1; ++j) {
-      const int tau = L - (kTaps - 1) + j;
-      if (tau >= 0) v[j] = x[((int64_t)b * L + tau) * a.x_stride + c];
-      else v[j] = ci ? ci[((int64_t)b * C + c) * (kTaps - 1) + tau + (kTaps - 1)] : io<T>::from(0.0f);
-    }
-    T* co = (T*)a.conv_out + ((int64_t)b * C + c) * (kTaps - 1);
-#pragma unroll
-    for (int j = 0; j < kTaps - 1; ++j) co[j] = v[j];
-  }
-}
-
-template <typename T>
 void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   auto mark = [&](int i) {
     if (marks) (void)hipEventRecord((hipEvent_t)marks[i], st);
@@ -152,8 +261,7 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   mark(0);
   if (a.P > 1) {
     dim3 gl(a.C / 64, a.P - 1, a.B);
-    hipLaunchKernelGGL(scan_local_kernel<T>, gl, dim3(64), 0, st, (const T*)a.xc, (const T*)a.delta, a.bc,
-                       (const T*)a.A_log, a.h0, a.loc, a.L, a.C, a.P, a.Lp);
+    hipLaunchKernelGGL((scan_pass_kernel<T, false>), gl, dim3(64), 0, st, a);
   }
   mark(1);
   if (a.P > 1) {
@@ -163,7 +271,7 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   }
   mark(2);
   dim3 gf(a.C / 64, a.P, a.B);
-  hipLaunchKernelGGL(scan_full_kernel<T>, gf, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((scan_pass_kernel<T, true>), gf, dim3(64), 0, st, a);
 }
 
 }  // namespace

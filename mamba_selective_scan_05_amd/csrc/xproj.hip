@@ -1,11 +1,15 @@
 // x_proj: dbc[m, n] = sum_k xc[m, k] * W[n, k]   (M tokens, N = dt_rank + 2*d_state, K = d_inner).
 //
-// bf16 path: matrix cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation.  A workgroup owns a 64-token
-// tile and the whole N; its waves split N into 16-wide tiles, so every xc element is read from HBM once.
-// The xc tile of each 64-wide K block is staged through LDS (double-buffered, rows padded by 16 bytes
-// against bank conflicts) and shared by the waves; each wave streams its own rows of W straight from
-// L2.  When there are too few token tiles to fill the GPU the K range is split over `splits` workgroups
-// that write fp32 partial sums; the norm step adds them in a fixed order, so results are deterministic.
+// bf16 path: matrix cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation.  A workgroup of 4 waves owns a
+// 128-token x 288-column output tile: wave (mg, ng) computes rows [64 mg, 64 mg + 64) x 16-wide column
+// tiles [9 ng, 9 ng + 9), so every xc element is read from HBM once and every W_x element once per
+// 128 tokens.  Both operands of each 64-wide K block are staged through LDS (double-buffered, rows
+// padded by 16 bytes against bank conflicts); the next block's global loads are in flight while the
+// current block's MFMAs run.  When there are too few token tiles to fill the GPU, the K range is split
+// over `splits` workgroups that write fp32 partial sums (added in a fixed order by the norm step, so the
+// result is deterministic).  Split s of token tile t runs as workgroup t * splits + s: workgroups are
+// handed to the 8 XCDs round-robin, so each XCD works on a fixed subset of K slices and keeps their
+// W_x rows in its own L2.  Wider projections (N > 288) run as several column groups (grid z).
 //
 // fp32 path: plain fp32 dot products on the vector ALU (the fp32 I/O mode must not round xc to bf16).
 #include "jm_device.h"
@@ -17,33 +21,38 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// 16 bytes in registers as a native vector (HIP's uint4 class does not always stay in registers when copied)
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
-constexpr int kMT = 64;          // tokens per workgroup tile
-constexpr int kKB = 64;          // K block staged in LDS
-constexpr int kLda = kKB + 8;    // padded LDS row, bf16 elements
-constexpr int kNT = 9;           // 16-wide N tiles per wave
+constexpr int kMT = 128;         // tokens per workgroup tile
+constexpr int kNG = 288;          // columns per workgroup (18 tiles of 16)
+constexpr int kKB = 64;           // K block staged in LDS
+constexpr int kLd = kKB + 8;      // padded LDS row, bf16 elements
+constexpr int kNT = 9;            // 16-wide column tiles per wave
+constexpr int kThreads = 256;
+constexpr int kAChunks = kMT * (kKB / 8) / kThreads;   // 16-byte chunks per thread: 4
+constexpr int kBChunks = kNG * (kKB / 8) / kThreads;   // 9
 
-__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t* p) {
-  uint4 raw = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(bf16x8, raw);
-}
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+__device__ __forceinline__ bf16x8 lds_frag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // MFMA 16x16x32 operand layout used here: lane l supplies row (l % 16) of A and column (l % 16) of B,
 // both over the 8 consecutive k values 8*(l / 16) .. +7 (the same k set for A and B, so the product is
 // independent of how the hardware orders k).  The accumulator holds rows 4*(l / 16) + i, column l % 16.
-__global__ __launch_bounds__(256) void xproj_mfma_kernel(const bf16_t* __restrict__ xc, const bf16_t* __restrict__ w,
-                                                         float* __restrict__ part, int M, int N, int K,
-                                                         int k_per_split) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][kMT * kLda];
+__global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __restrict__ xc,
+                                                              const bf16_t* __restrict__ w,
+                                                              float* __restrict__ part, int M, int N, int K,
+                                                              int splits) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][kMT * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kNG * kLd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nthreads = blockDim.x;
-  const int m0 = blockIdx.x * kMT;
-  const int s = blockIdx.y;
-  const int kbeg = s * k_per_split;
-  const int nblocks = k_per_split / kKB;
+  const int s = blockIdx.x % splits;
+  const int m0 = (blockIdx.x / splits) * kMT;
+  const int n0 = blockIdx.z * kNG;
+  const int kps = K / splits;
+  const int kbeg = s * kps;
+  const int nblocks = kps / kKB;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int mg = wave & 1, ng = wave >> 1;
 
   f32x4 acc[4][kNT];
 #pragma unroll
@@ -51,50 +60,102 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(const bf16_t* __restric
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A tile loader: 64 rows x 64 k = 512 chunks of 16 bytes.
-  auto load_a = [&](int kb, int buf) {
-    for (int q = tid; q < kMT * (kKB / 8); q += nthreads) {
-      const int row = q >> 3, kc = (q & 7) * 8;
-      const int m = m0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < M) v = *reinterpret_cast<const uint4*>(xc + (int64_t)m * K + kb + kc);
-      *reinterpret_cast<uint4*>(&As[buf][row * kLda + kc]) = v;
-    }
-  };
-
-  const int ntile0 = wave * kNT;
-  load_a(kbeg, 0);
+  // xc (from HBM) is loaded two K blocks ahead, W_x (from L2) one block ahead.  Rows past M (tokens) or
+  // N (columns) are clamped to the last valid row: they only feed outputs that are never stored, and
+  // branch-free loads let the memory counter be waited on precisely.
+  // Per-thread chunk addresses: chunk q of a block is row (tid + q * 256) / 8, k offset ((tid + q*256) % 8)*8.
+  const int kc = (tid & 7) * 8;
+  const bf16_t* pa[kAChunks];
+  const bf16_t* pb[kBChunks];
+  int la[kAChunks], lb[kBChunks];
+#pragma unroll
+  for (int q = 0; q < kAChunks; ++q) {
+    const int row = (tid >> 3) + q * (kThreads / 8);
+    pa[q] = xc + (int64_t)min(m0 + row, M - 1) * K + kc;
+    la[q] = row * kLd + kc;
+  }
+#pragma unroll
+  for (int q = 0; q < kBChunks; ++q) {
+    const int row = (tid >> 3) + q * (kThreads / 8);
+    pb[q] = w + (int64_t)min(n0 + row, N - 1) * K + kc;
+    lb[q] = row * kLd + kc;
+  }
+  // K blocks go in pairs (even block from LDS buffer 0, odd from buffer 1) with two register sets for xc
+  // (X, Y), so a prefetched block never has to be copied between registers.  While block b computes:
+  // W_x of b + 1 and xc of b + 2 are requested (W_x first: the memory counter drains in issue order, so
+  // the LDS store at the end of the block waits for W_x and the older xc only); afterwards xc of b + 1
+  // (already in registers) and W_x of b + 1 go to the other LDS buffer.  Loads past the last block re-read
+  // it, and the LDS stores are unconditional (the last one fills the idle buffer): conditional loads or
+  // stores would let the compiler sink the loads past the MFMAs.
+  u32x4 rx[kAChunks], ry[kAChunks], rb[kBChunks];
+  auto blk = [&](int b) { return kbeg + min(b, nblocks - 1) * kKB; };
+#pragma unroll
+  for (int q = 0; q < kAChunks; ++q) ry[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(0));
+#pragma unroll
+  for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const u32x4*>(pb[q] + blk(0));
+#pragma unroll
+  for (int q = 0; q < kAChunks; ++q) rx[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(1));
+#pragma unroll
+  for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<u32x4*>(&As[0][la[q]]) = ry[q];
+#pragma unroll
+  for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<u32x4*>(&Bs[0][lb[q]]) = rb[q];
   __syncthreads();
-  for (int ib = 0; ib < nblocks; ++ib) {
-    const int kb = kbeg + ib * kKB;
-    const int buf = ib & 1;
-    if (ib + 1 < nblocks) load_a(kb + kKB, buf ^ 1);
+
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kKB; ks += 32) {
       bf16x8 a[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = *reinterpret_cast<const bf16x8*>(&As[buf][(r * 16 + lr) * kLda + ks + lk]);
+      for (int r = 0; r < 4; ++r) a[r] = lds_frag(&As[buf][(mg * 64 + r * 16 + lr) * kLd + ks + lk]);
 #pragma unroll
       for (int t = 0; t < kNT; ++t) {
-        const int n = (ntile0 + t) * 16 + lr;
-        const bf16x8 bv = n < N ? ld_bf16x8(w + (int64_t)n * K + kb + ks + lk) : zero_bf16x8();
+        const bf16x8 bv = lds_frag(&Bs[buf][((ng * kNT + t) * 16 + lr) * kLd + ks + lk]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bv, acc[r][t], 0, 0, 0);
       }
     }
+  };
+
+  for (int ib = 0; ib < nblocks; ib += 2) {
+    // even block ib (buffer 0); rx holds xc of ib + 1
+#pragma unroll
+    for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const u32x4*>(pb[q] + blk(ib + 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kAChunks; ++q) ry[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(ib + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+#pragma unroll
+    for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<u32x4*>(&As[1][la[q]]) = rx[q];
+#pragma unroll
+    for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<u32x4*>(&Bs[1][lb[q]]) = rb[q];
+    __syncthreads();
+    if (ib + 1 >= nblocks) break;
+    // odd block ib + 1 (buffer 1); ry holds xc of ib + 2
+#pragma unroll
+    for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const u32x4*>(pb[q] + blk(ib + 2));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kAChunks; ++q) rx[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(ib + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+#pragma unroll
+    for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<u32x4*>(&As[0][la[q]]) = ry[q];
+#pragma unroll
+    for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<u32x4*>(&Bs[0][lb[q]]) = rb[q];
     __syncthreads();
   }
 
   float* dst = part + (int64_t)s * M * N;
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
-    const int n = (ntile0 + t) * 16 + lr;
+    const int n = n0 + (ng * kNT + t) * 16 + lr;
     if (n >= N) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + r * 16 + (lane >> 4) * 4 + i;
+        const int m = m0 + mg * 64 + r * 16 + (lane >> 4) * 4 + i;
         if (m < M) dst[(int64_t)m * N + n] = acc[r][t][i];
       }
   }
@@ -120,15 +181,15 @@ __global__ __launch_bounds__(64) void xproj_f32_kernel(const float* __restrict__
 
 }  // namespace
 
+int xproj_token_tile() { return kMT; }
+
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
                   hipStream_t st) {
   if (M == 0) return;
   if (bf16) {
-    const int ntiles = (N + 15) / 16;
-    const int waves = (ntiles + kNT - 1) / kNT;
-    dim3 grid((M + kMT - 1) / kMT, splits);
-    hipLaunchKernelGGL(xproj_mfma_kernel, grid, dim3(64 * waves), 0, st, (const bf16_t*)xc, (const bf16_t*)w,
-                       part, M, N, K, K / splits);
+    dim3 grid(((M + kMT - 1) / kMT) * splits, 1, (N + kNG - 1) / kNG);
+    hipLaunchKernelGGL(xproj_mfma_kernel, grid, dim3(kThreads), 0, st, (const bf16_t*)xc, (const bf16_t*)w, part,
+                       M, N, K, splits);
   } else {
     dim3 grid(M, (N + 63) / 64);
     hipLaunchKernelGGL(xproj_f32_kernel, grid, dim3(64), 0, st, (const float*)xc, (const float*)w, part, M, N, K);

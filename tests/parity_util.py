@@ -42,12 +42,16 @@ def err_stats(got, ref) -> Dict[str, float]:
             "finite": bool(np.isfinite(g).all())}
 
 
-def assert_close(name: str, got, ref, io_dtype: str) -> Dict[str, float]:
+def assert_close(name: str, got, ref, io_dtype: str, magnitude_scaled: bool = False) -> Dict[str, float]:
+    """fp32: max abs error <= 1e-4 (the workloads' outputs are O(1)).  With magnitude_scaled (stress cases
+    whose outputs reach hundreds, where fp32 rounding alone exceeds 1e-4 absolute) the bound is
+    1e-4 * max(1, max |ref|), i.e. 1e-4 relative to the largest reference value."""
     s = err_stats(got, ref)
     log(f"  {name}: max_abs={s['max_abs']:.3e} max_ref={s['max_ref']:.3e} rel={s['rel']:.3e}")
     assert s["finite"], f"{name}: non-finite values"
     if io_dtype == "f32":
-        assert s["max_abs"] <= F32_ATOL, f"{name}: max abs error {s['max_abs']:.3e} > {F32_ATOL}"
+        tol = F32_ATOL * (max(1.0, s["max_ref"]) if magnitude_scaled else 1.0)
+        assert s["max_abs"] <= tol, f"{name}: max abs error {s['max_abs']:.3e} > {tol:.3e}"
     else:
         assert s["rel"] <= BF16_RTOL, f"{name}: relative error {s['rel']:.3e} > {BF16_RTOL}"
     return s

@@ -38,7 +38,7 @@ def _small(name, B, L, C, R, io, seed, **kw):
     return MixerConfig(name, batch=B, seqlen=L, d_inner=C, dt_rank=R, io_dtype=io, seed=seed, **kw)
 
 
-def _run_and_check(cfg, with_state=True, row_stride=None, w=None, check_label=""):
+def _run_and_check(cfg, with_state=True, row_stride=None, w=None, check_label="", magnitude_scaled=False):
     w = w if w is not None else make_weights(cfg, DEV)
     a = make_activations(cfg, DEV, row_stride=row_stride)
     st = make_state(cfg, DEV) if with_state else {"conv_state": None, "ssm_state": None}
@@ -49,8 +49,8 @@ def _run_and_check(cfg, with_state=True, row_stride=None, w=None, check_label=""
     w64 = weights_f64(w)
     h0 = None if st["ssm_state"] is None else to_f64(st["ssm_state"])
     ro, rc, rh = oracle_prefill(cfg, w64, a["x"], a["z"], st["conv_state"], h0)
-    assert_close("out", out, ro, cfg.io_dtype)
-    assert_close("h_final", hs, rh, cfg.io_dtype)
+    assert_close("out", out, ro, cfg.io_dtype, magnitude_scaled)
+    assert_close("h_final", hs, rh, cfg.io_dtype, magnitude_scaled)
     assert_bitwise("conv_state", cs, torch.from_numpy(rc).to(cfg.torch_dtype))
     return m, out, cs, hs
 
@@ -103,7 +103,8 @@ def test_slow_decay_carries_and_scan_term_alone(io):
     import mamba_selective_scan_05_amd as jm
     lay = jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen))
     assert lay.scan_chunks > 1
-    _run_and_check(cfg, w=w)
+    # slow decay lets the state grow to |out| ~ 400: the fp32 bound is taken relative to that magnitude
+    _run_and_check(cfg, w=w, magnitude_scaled=True)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
