@@ -41,19 +41,12 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 // SiLU(u) = u / (1 + e^-u).  For u -> -inf the exp overflows to inf and the reciprocal gives 0.
 __device__ __forceinline__ float silu(float u) { return u * rcp_fast(1.0f + exp2_fast(-u * kLog2e)); }
 
-// log(1 + e) for e in [0, 1], accurate to a few ulp also for tiny e: the rounding of 1 + e is undone by
-// scaling log(u) with e / (u - 1) (the standard correction for log1p).
-__device__ __forceinline__ float log1p_small(float e) {
-  float u = 1.0f + e;
-  float d = u - 1.0f;
-  float l = __builtin_amdgcn_logf(u) * kLn2;  // v_log_f32 is log2
-  return d == 0.0f ? e : l * (e / d);
-}
-
-// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|), without overflow.
+// softplus(v) = log(1 + e^v) = max(v, 0) + log(1 + e^-|v|), without overflow, on the transcendental unit
+// (v_exp_f32, v_log_f32).  For v below about -17, 1 + e^v rounds to 1 and the result is 0 instead of
+// e^v < 4e-8: an absolute error far below anything a delta of that size can change downstream.
 __device__ __forceinline__ float softplus(float v) {
-  float e = exp2_fast(-fabsf(v) * kLog2e);
-  return fmaxf(v, 0.0f) + log1p_small(e);
+  const float e = exp2_fast(-fabsf(v) * kLog2e);
+  return fmaxf(v, 0.0f) + __builtin_amdgcn_logf(1.0f + e) * kLn2;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -191,6 +191,107 @@ __global__ __launch_bounds__(256, 2) void dtproj_mfma_kernel(const bf16_t* __res
   }
 }
 
+// dt_rank <= 256: persistent workgroups.  Each of the 4 waves holds the W_dt rows of its 64 channels for
+// the whole K (dt_rank) in registers and walks a contiguous range of 64-token tiles; the dln tiles stream
+// through double-buffered LDS (the next tile's loads are in flight while the current one multiplies) and
+// each wave transposes its 64 x 64 output tile through its own LDS region for 16-byte stores.  Workgroup
+// i runs on XCD i % 8 and takes token-tile group i % G, so each XCD keeps its group's dln tiles in its L2.
+constexpr int kDtLdsA = 2 * 64 * kDtLd * 2;              // two dln tiles (bytes)
+constexpr int kDtLdsO = 4 * 64 * kDtOutLd * 2;           // four per-wave output tiles (bytes)
+__global__ __launch_bounds__(256, 1) void dtproj_mfma_stream_kernel(const bf16_t* __restrict__ dln,
+                                                                    const bf16_t* __restrict__ w,
+                                                                    const bf16_t* __restrict__ bias,
+                                                                    bf16_t* __restrict__ delta, int M, int C, int R,
+                                                                    int groups, int tiles_per_group) {
+  __shared__ __attribute__((aligned(16))) char lds[kDtLdsA + kDtLdsO];
+  bf16_t* As = reinterpret_cast<bf16_t*>(lds);                       // [2][64 * kDtLd]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  bf16_t* os = reinterpret_cast<bf16_t*>(lds + kDtLdsA) + wave * 64 * kDtOutLd;
+  const int nmt = (M + 63) / 64;
+  const int g = blockIdx.x % groups, cb = blockIdx.x / groups;
+  const int mt_beg = g * tiles_per_group, mt_end = min(nmt, mt_beg + tiles_per_group);
+  if (mt_beg >= mt_end) return;                      // uniform over the workgroup
+  const int c0 = cb * 256 + wave * 64;
+  const bool active = c0 < C;
+  const int cw = active ? c0 : 0;                    // waves past C read valid rows and store nothing
+
+  // this wave's W_dt fragments for all of K (zero past dt_rank)
+  bf16x8 b[kDtMaxR / 32][4];
+#pragma unroll
+  for (int ks = 0; ks < kDtMaxR / 32; ++ks)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[ks][t] = ld16_guard(w + (int64_t)(cw + t * 16 + lr) * R + ks * 32 + lk, ks * 32 + lk < R);
+  float bs[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bs[t] = bf2f(bias[cw + t * 16 + lr]);
+
+  // dln tile loader: 64 rows x 256 k = 2048 chunks of 16 bytes, 8 per thread; rows past M and k past R
+  // read as zero
+  typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+  auto load_tile = [&](int mt, u32x4* r) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int id = tid + q * 256, row = id >> 5, kc = (id & 31) * 8;
+      const int m = min(mt * 64 + row, M - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(dln + (int64_t)m * R + min(kc, R - 8));
+      r[q] = (kc < R && mt * 64 + row < M) ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf, const u32x4* r) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int id = tid + q * 256, row = id >> 5, kc = (id & 31) * 8;
+      *reinterpret_cast<u32x4*>(&As[buf * 64 * kDtLd + row * kDtLd + kc]) = r[q];
+    }
+  };
+  u32x4 rt[8];
+  load_tile(mt_beg, rt);
+  store_tile(0, rt);
+  __syncthreads();
+  int buf = 0;
+  for (int mt = mt_beg; mt < mt_end; ++mt) {
+    load_tile(min(mt + 1, mt_end - 1), rt);          // next tile in flight (the last one re-reads itself)
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16_t* At = As + buf * 64 * kDtLd;
+#pragma unroll
+    for (int ks = 0; ks < kDtMaxR / 32; ++ks) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = *reinterpret_cast<const bf16x8*>(&At[(r * 16 + lr) * kDtLd + ks * 32 + lk]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b[ks][t], acc[r][t], 0, 0, 0);
+    }
+    // epilogue: bias + softplus -> bf16 -> this wave's LDS tile -> 16-byte rows.  One wave's LDS accesses
+    // complete in order, so the read-back sees the writes.
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+          os[(r * 16 + (lane >> 4) * 4 + i2) * kDtOutLd + t * 16 + lr] = f2bf(softplus(acc[r][t][i2] + bs[t]));
+    if (active) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int id = lane + 64 * q, row = id >> 3, cc = (id & 7) * 8;
+        const int m = mt * 64 + row;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&os[row * kDtOutLd + cc]);
+        if (m < M) *reinterpret_cast<u32x4*>(delta + (int64_t)m * C + c0 + cc) = v;
+      }
+    }
+    store_tile(buf ^ 1, rt);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
 __global__ __launch_bounds__(256) void dtproj_f32_kernel(const float* __restrict__ dln, const float* __restrict__ w,
                                                          const float* __restrict__ bias, float* __restrict__ delta,
                                                          int M, int C, int R) {
@@ -221,8 +322,18 @@ void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, voi
   if (M == 0) return;
   if (bf16) {
     const int ncb = (C + 255) / 256, nmt = (M + 63) / 64;
-    hipLaunchKernelGGL(dtproj_mfma_kernel, dim3(ncb * nmt), dim3(256), 0, st, (const bf16_t*)dln, (const bf16_t*)w,
-                       (const bf16_t*)b, (bf16_t*)delta, M, C, R);
+    if (R <= kDtMaxR) {
+      // one workgroup per CU: enough token-tile groups for ~256 workgroups, 8 when possible (one per XCD)
+      int groups = ncb >= 256 ? 1 : 256 / ncb;
+      if (groups > 8) groups = groups / 8 * 8;
+      if (groups > nmt) groups = nmt;
+      const int per = (nmt + groups - 1) / groups;
+      hipLaunchKernelGGL(dtproj_mfma_stream_kernel, dim3(ncb * groups), dim3(256), 0, st, (const bf16_t*)dln,
+                         (const bf16_t*)w, (const bf16_t*)b, (bf16_t*)delta, M, C, R, groups, per);
+    } else {
+      hipLaunchKernelGGL(dtproj_mfma_kernel, dim3(ncb * nmt), dim3(256), 0, st, (const bf16_t*)dln, (const bf16_t*)w,
+                         (const bf16_t*)b, (bf16_t*)delta, M, C, R);
+    }
   } else {
     dim3 grid((C + 255) / 256, M);
     hipLaunchKernelGGL(dtproj_f32_kernel, grid, dim3(256), 0, st, (const float*)dln, (const float*)w,

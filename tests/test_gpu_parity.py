@@ -70,6 +70,14 @@ def test_ragged_multi_piece(io):
     _run_and_check(cfg)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_largest_dt_rank(io):
+    # dt_rank 512 (the largest supported): x_proj runs as two column groups and dt_proj takes its
+    # general path (the K loop over dt_rank slices)
+    cfg = _small(f"rank512_{io}", 2, 300, 256, 512, io, 20)
+    _run_and_check(cfg)
+
+
 def test_bf16_wide_strided_views():
     # x and z as strided halves of one [B, L, 2C + 64] buffer, as an in_proj output holds them
     cfg = _small("bf16_strided", 2, 333, 512, 64, "bf16", 12)
