@@ -89,6 +89,24 @@ def decode_bytes(B, C, N, R, K, esize):
     return B * C * per + weights
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary under
+    profiles/, or None when there is none for this workload or the kernel sources changed since it was taken
+    (the summary records the sha256 of the sources it measured)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_B1_L4096_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    meta = json.load(open(path))
+    if meta.get("workload") != workload or meta.get("kernel") != kernel:
+        return None
+    src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in meta["sources"])
+    if hashlib.sha256(src).hexdigest() != meta["source_sha256"]:
+        return None
+    return int(meta["bytes_per_launch"])
+
+
 def stage_groups(stage_ms):
     return {
         "conv_silu": stage_ms["conv_silu"],
@@ -247,6 +265,20 @@ def cpu_baseline(cfg, max_tokens):
                       f"C={cfg.d_inner}), {dt:.1f} s; matmuls on {blas} BLAS threads, the scan single-threaded"}
 
 
+def run_decode(jm, dcfg, args, hip):
+    log(f"decode {dcfg.name}: warmup {args.warmup}, steps {args.steps}")
+    dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
+    db = decode_bytes(dcfg.batch, dcfg.d_inner, dcfg.d_state, dcfg.dt_rank, dcfg.d_conv, 2)
+    gbs = db / (dec["ms"] * 1e-3) / 1e9
+    for k, t in dec["stage_ms"].items():
+        log(f"  {k:12s} {t * 1e3:9.2f} us")
+    return {"workload": f"{dcfg.name}: one token per sequence, state rotated over {N_STATE_SETS} sets",
+            "batch": dcfg.batch, "us_per_step": round(dec["ms"] * 1e3, 2),
+            "tokens_per_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "alg_bytes": db,
+            "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +287,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--config", type=int, default=1, choices=(1, 2, 3),
+                    help="prefill workload: 1 = B1 L4096 (default), 2 = B8 L4096, 3 = B1 L262144")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode workload and print its figures (for per-workload profiles)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run three device copies of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -272,7 +310,17 @@ def main():
         sys.exit(1)
     jm.lib()
     hip = Hip()
-    cfg = CONFIGS[1]
+    if args.copy_calibration:
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.decode_only:
+        print(json.dumps({"decode": run_decode(jm, CONFIGS[4], args, hip)}), flush=True)
+        return
+    cfg = CONFIGS[args.config]
     log(f"prefill {cfg.name}: warmup {args.warmup}, steps {args.steps}")
     pre = time_prefill(jm, cfg, args.steps, args.warmup, hip)
     B, L, C, N, R = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dt_rank
@@ -309,23 +357,13 @@ def main():
                    "d_inner": C, "d_state": N, "dt_rank": R, "d_conv": cfg.d_conv, "io": "bf16",
                    "state": "fp32", "x_proj_splits": pre["splits"], "scan_pieces": pre["pieces"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
+                     "alg_bytes_per_launch": alg[dom], "us_per_launch": stages[dom]["us"]},
         "stages": stages,
         "mixer_GB_s": round(sum(alg.values()) / (pre["ms"] * 1e-3) / 1e9, 1),
     }
     if not args.no_decode:
-        dcfg = CONFIGS[4]
-        log(f"decode {dcfg.name}: warmup {args.warmup}, steps {args.steps}")
-        dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
-        db = decode_bytes(dcfg.batch, dcfg.d_inner, dcfg.d_state, dcfg.dt_rank, dcfg.d_conv, 2)
-        gbs = db / (dec["ms"] * 1e-3) / 1e9
-        for k, t in dec["stage_ms"].items():
-            log(f"  {k:12s} {t * 1e3:9.2f} us")
-        result["decode"] = {"workload": f"{dcfg.name}: one token per sequence, state rotated over {N_STATE_SETS} sets",
-                            "batch": dcfg.batch, "us_per_step": round(dec["ms"] * 1e3, 2),
-                            "tokens_per_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "alg_bytes": db,
-                            "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                            "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()}}
+        result["decode"] = run_decode(jm, CONFIGS[4], args, hip)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {min(args.cpu_tokens, cfg.seqlen)} tokens ...")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)

@@ -14,7 +14,10 @@ constexpr int kMaxR = 512;   // dt_rank bound of the norm kernel
 constexpr int64_t kAlign = 256;
 
 // Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.
-constexpr int64_t kScanWaveTarget = 4096;
+#ifndef JM_SCAN_WAVE_TARGET
+#define JM_SCAN_WAVE_TARGET 6144
+#endif
+constexpr int64_t kScanWaveTarget = JM_SCAN_WAVE_TARGET;
 constexpr int kMinPiece = 128;
 // x_proj: split the contraction over channel slices until there are this many workgroups (one per CU).
 constexpr int kXprojWgTarget = 256;

@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kN = 16;
 constexpr int kTaps = 4;
-constexpr int kBatch = 8;   // tokens per prefetch batch
+constexpr int kBatch = 4;   // tokens per prefetch batch (keeps the pass under 128 VGPRs: 4 waves per SIMD)
 
 // Buffer resource over [base, base + bytes): raw (untyped) accesses, 32-bit byte offsets.
 constexpr int kBufferFlags = 0x00020000;   // dword 3 of a raw buffer descriptor on gfx9-family GPUs
@@ -239,16 +239,29 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
   const int c = (int)(i % C);
   const int n = (int)((i / C) % kN);
   const int b = (int)(i / ((int64_t)C * kN));
-  const float a2 = -expf(io<T>::ld(A_log + (int64_t)c * kN + n)) * kLog2e;
+  const float a2 = -exp2_fast(io<T>::ld(A_log + (int64_t)c * kN + n) * kLog2e) * kLog2e;
   const float* lb = loc + (int64_t)b * P * (kN + 1) * C;
   float* cb = cin + (int64_t)b * P * kN * C;
   cb[(int64_t)n * C + c] = h0 ? h0[((int64_t)b * C + c) * kN + n] : 0.0f;
   float H = lb[(int64_t)n * C + c];   // piece 0 started from h0: its end state is exact
-  for (int p = 1; p < P; ++p) {
-    cb[((int64_t)p * kN + n) * C + c] = H;
-    if (p + 1 < P) {
+  // pieces in groups of 8: all loads of a group are issued before its serial combine
+  constexpr int kG = 8;
+  for (int p0 = 1; p0 < P; p0 += kG) {
+    float hl[kG], sd[kG];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const int p = min(p0 + j, P - 1);
       const float* lp = lb + (int64_t)p * (kN + 1) * C;
-      H = fmaf(exp2_fast(lp[(int64_t)kN * C + c] * a2), H, lp[(int64_t)n * C + c]);
+      hl[j] = lp[(int64_t)n * C + c];
+      sd[j] = lp[(int64_t)kN * C + c];
+    }
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const int p = p0 + j;
+      if (p < P) {
+        cb[((int64_t)p * kN + n) * C + c] = H;
+        H = fmaf(exp2_fast(sd[j] * a2), H, hl[j]);   // unused after the last piece
+      }
     }
   }
 }
