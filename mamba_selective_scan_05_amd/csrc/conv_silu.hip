@@ -82,11 +82,21 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T* __restrict__ x,
   // prev[j] = extended input at t - 3 + j
   float prev[kTaps - 1][V];
   if (t0 == 0) {
+    if (conv_in) {
+      // the state of these V channels is 3V contiguous elements (48 bytes): three 16-byte loads
+      float st[(kTaps - 1) * V];
 #pragma unroll
-    for (int i = 0; i < V; ++i)
+      for (int q = 0; q < kTaps - 1; ++q) load16(conv_in + ((int64_t)b * C + c0) * (kTaps - 1) + q * V, st + q * V);
 #pragma unroll
-      for (int j = 0; j < kTaps - 1; ++j)
-        prev[j][i] = conv_in ? io<T>::ld(conv_in + ((int64_t)b * C + c0 + i) * (kTaps - 1) + j) : 0.0f;
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int j = 0; j < kTaps - 1; ++j) prev[j][i] = st[i * (kTaps - 1) + j];
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int j = 0; j < kTaps - 1; ++j) prev[j][i] = 0.0f;
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < kTaps - 1; ++j) load16(x + ((int64_t)b * L + t0 - (kTaps - 1) + j) * xs + c0, prev[j]);

@@ -80,6 +80,10 @@ Plan make_plan(const jm_mixer_dims* d, bool decode) {
   int64_t want = (kScanWaveTarget + waves - 1) / waves;
   int64_t lp = p.L > 0 ? (p.L + want - 1) / want : 1;
   if (lp < kMinPiece) lp = kMinPiece;
+  // the scan addresses a piece through 32-bit byte offsets: keep each piece's rows under 2 GiB
+  const int64_t row_bytes = (p.xs > p.zs ? (p.xs > p.C ? p.xs : p.C) : (p.zs > p.C ? p.zs : p.C)) * p.esize;
+  const int64_t max_rows = ((int64_t)1 << 31) / row_bytes - 1;
+  if (lp > max_rows) lp = max_rows;
   p.Lp = (int)(lp < p.L ? lp : (p.L > 0 ? p.L : 1));
   p.P = p.L > 0 ? (int)((p.L + p.Lp - 1) / p.Lp) : 1;
 

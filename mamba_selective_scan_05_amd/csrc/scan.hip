@@ -29,6 +29,8 @@ namespace {
 constexpr int kN = 16;
 constexpr int kTaps = 4;
 constexpr int kBatch = 4;   // tokens per prefetch batch (keeps the pass under 128 VGPRs: 4 waves per SIMD)
+// s_waitcnt operand (gfx9 encoding): scalar-memory count 0, vector-memory and export counts at their maxima
+constexpr int kWaitScalar = 0xC07F;
 
 // Buffer resource over [base, base + bytes): raw (untyped) accesses, 32-bit byte offsets.
 constexpr int kBufferFlags = 0x00020000;   // dword 3 of a raw buffer descriptor on gfx9-family GPUs
@@ -146,34 +148,33 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
       sdt += dt;
     }
   };
+  // B / C of the token being computed, fetched one token ahead.  Scalar loads may complete out of order,
+  // so the only wait for them is "all scalar loads done": each token first waits for its own B / C, then
+  // requests the next token's, then computes, and the request stays in flight for a whole token.
+  float Bc[kN], Cc[kN];
+  auto load_bc = [&](int i, float* Bt, float* Ct) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      Bt[n] = bcp[(int64_t)i * (2 * kN) + n];
+      Ct[n] = FULL ? bcp[(int64_t)i * (2 * kN) + kN + n] : 0.0f;
+    }
+  };
   // a batch of kBatch tokens starting at i0 whose inputs are in d/x/z; count < kBatch only for the last
   auto run_batch = [&](int i0, const R* d, const R* x, const R* z) {
     const int count = min(kBatch, n_tok - i0);
     if (count == kBatch) {
-      float Bc[kN], Cc[kN];
-#pragma unroll
-      for (int n = 0; n < kN; ++n) {
-        Bc[n] = bcp[(int64_t)i0 * (2 * kN) + n];
-        Cc[n] = FULL ? bcp[(int64_t)i0 * (2 * kN) + kN + n] : 0.0f;
-      }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        // B / C of the next token are requested before this token's arithmetic
+        __builtin_amdgcn_s_waitcnt(kWaitScalar);
+        __builtin_amdgcn_sched_barrier(0);
         float Bn[kN], Cn[kN];
-        if (j + 1 < kBatch) {
-#pragma unroll
-          for (int n = 0; n < kN; ++n) {
-            Bn[n] = bcp[(int64_t)(i0 + j + 1) * (2 * kN) + n];
-            Cn[n] = FULL ? bcp[(int64_t)(i0 + j + 1) * (2 * kN) + kN + n] : 0.0f;
-          }
-        }
+        load_bc(min(i0 + j + 1, n_tok - 1), Bn, Cn);   // clamped: the last token re-reads its own row
+        __builtin_amdgcn_sched_barrier(0);
         step(i0 + j, d[j], x[j], z[j], Bc, Cc);
-        if (j + 1 < kBatch) {
 #pragma unroll
-          for (int n = 0; n < kN; ++n) {
-            Bc[n] = Bn[n];
-            Cc[n] = Cn[n];
-          }
+        for (int n = 0; n < kN; ++n) {
+          Bc[n] = Bn[n];
+          Cc[n] = Cn[n];
         }
       }
     } else {
@@ -181,11 +182,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
       for (int j = 0; j < kBatch; ++j) {
         if (j >= count) break;
         float Bt[kN], Ct[kN];
-#pragma unroll
-        for (int n = 0; n < kN; ++n) {
-          Bt[n] = bcp[(int64_t)(i0 + j) * (2 * kN) + n];
-          Ct[n] = FULL ? bcp[(int64_t)(i0 + j) * (2 * kN) + kN + n] : 0.0f;
-        }
+        load_bc(i0 + j, Bt, Ct);
         step(i0 + j, d[j], x[j], z[j], Bt, Ct);
       }
     }
@@ -193,12 +190,17 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
 
   // ping-pong buffers: batch k computes from one set while batch k+1 loads into the other
   R dA[kBatch], xA[kBatch], zA[kBatch], dB[kBatch], xB[kBatch], zB[kBatch];
-  if (n_tok > 0) load_batch(0, dA, xA, zA);
+  if (n_tok > 0) {
+    load_batch(0, dA, xA, zA);
+    load_bc(0, Bc, Cc);
+  }
+  // The prefetches are unconditional (clamped rows): a conditional one would make the compiler's wait at
+  // the join assume the no-prefetch path, i.e. wait for the loads just issued.
   for (int i0 = 0; i0 < n_tok; i0 += 2 * kBatch) {
-    if (i0 + kBatch < n_tok) load_batch(i0 + kBatch, dB, xB, zB);
+    load_batch(i0 + kBatch, dB, xB, zB);
     run_batch(i0, dA, xA, zA);
     if (i0 + kBatch >= n_tok) break;
-    if (i0 + 2 * kBatch < n_tok) load_batch(i0 + 2 * kBatch, dA, xA, zA);
+    load_batch(i0 + 2 * kBatch, dA, xA, zA);
     run_batch(i0 + kBatch, dB, xB, zB);
   }
 
