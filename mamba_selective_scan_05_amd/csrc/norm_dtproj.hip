@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
 }
 
 constexpr int kDtMaxR = 256;            // dt_rank of the staged bf16 path (larger ranks loop in slices)
-constexpr int kDtLd = kDtMaxR + 8;      // padded LDS row of the dln tile
+constexpr int kDtLd = kDtMaxR + 16;     // padded LDS row of the dln tile (32 bytes of pad: conflict-free fragment reads)
 constexpr int kDtOutLd = 64 + 8;        // padded LDS row of a wave's output tile (bf16)
 
 __device__ __forceinline__ bf16x8 ld16_guard(const bf16_t* p, bool ok) {
@@ -191,72 +191,85 @@ __global__ __launch_bounds__(256, 2) void dtproj_mfma_kernel(const bf16_t* __res
   }
 }
 
-// dt_rank <= 256: persistent workgroups.  Each of the 4 waves holds the W_dt rows of its 64 channels for
-// the whole K (dt_rank) in registers and walks a contiguous range of 64-token tiles; the dln tiles stream
-// through double-buffered LDS (the next tile's loads are in flight while the current one multiplies) and
-// each wave transposes its 64 x 64 output tile through its own LDS region for 16-byte stores.  Workgroup
-// i runs on XCD i % 8 and takes token-tile group i % G, so each XCD keeps its group's dln tiles in its L2.
+// dt_rank <= 256: persistent workgroups of 8 waves (two per SIMD).  Each wave holds the W_dt rows of its 32
+// channels for the whole K (dt_rank) in registers and walks a contiguous range of 64-token tiles; the dln
+// tiles stream through double-buffered LDS (the next tile's loads are in flight while the current one
+// multiplies).  W_dt is the A operand and the dln tile the B operand, so a lane's accumulator holds four
+// consecutive channels of one token and leaves as one 8-byte store, with no transpose.  Workgroup i runs
+// on XCD i % 8 and takes token-tile group i % G, so each XCD keeps its group's dln tiles in its L2.
+constexpr int kDtStreamWaves = 8;
+constexpr int kDtStreamThreads = 64 * kDtStreamWaves;
+constexpr int kDtWaveCh = 256 / kDtStreamWaves;         // channels per wave
+constexpr int kDtWaveT = kDtWaveCh / 16;                 // 16-channel MFMA tiles per wave
 constexpr int kDtLdsA = 2 * 64 * kDtLd * 2;              // two dln tiles (bytes)
-constexpr int kDtLdsO = 4 * 64 * kDtOutLd * 2;           // four per-wave output tiles (bytes)
-__global__ __launch_bounds__(256, 1) void dtproj_mfma_stream_kernel(const bf16_t* __restrict__ dln,
-                                                                    const bf16_t* __restrict__ w,
-                                                                    const bf16_t* __restrict__ bias,
-                                                                    bf16_t* __restrict__ delta, int M, int C, int R,
-                                                                    int groups, int tiles_per_group) {
-  __shared__ __attribute__((aligned(16))) char lds[kDtLdsA + kDtLdsO];
-  bf16_t* As = reinterpret_cast<bf16_t*>(lds);                       // [2][64 * kDtLd]
+__global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel(const bf16_t* __restrict__ dln,
+                                                                               const bf16_t* __restrict__ w,
+                                                                               const bf16_t* __restrict__ bias,
+                                                                               bf16_t* __restrict__ delta, int M,
+                                                                               int C, int R, int groups,
+                                                                               int tiles_per_group) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2 * 64 * kDtLd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-  bf16_t* os = reinterpret_cast<bf16_t*>(lds + kDtLdsA) + wave * 64 * kDtOutLd;
+  const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
   const int nmt = (M + 63) / 64;
   const int g = blockIdx.x % groups, cb = blockIdx.x / groups;
   const int mt_beg = g * tiles_per_group, mt_end = min(nmt, mt_beg + tiles_per_group);
   if (mt_beg >= mt_end) return;                      // uniform over the workgroup
-  const int c0 = cb * 256 + wave * 64;
+  const int c0 = cb * 256 + wave * kDtWaveCh;
   const bool active = c0 < C;
   const int cw = active ? c0 : 0;                    // waves past C read valid rows and store nothing
 
-  // this wave's W_dt fragments for all of K (zero past dt_rank)
-  bf16x8 b[kDtMaxR / 32][4];
+  // this wave's W_dt fragments for all of K (zero past dt_rank): A operand, row = channel, 8 k per lane
+  bf16x8 wa[kDtMaxR / 32][kDtWaveT];
 #pragma unroll
   for (int ks = 0; ks < kDtMaxR / 32; ++ks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b[ks][t] = ld16_guard(w + (int64_t)(cw + t * 16 + lr) * R + ks * 32 + lk, ks * 32 + lk < R);
-  float bs[4];
+    for (int t = 0; t < kDtWaveT; ++t)
+      wa[ks][t] = ld16_guard(w + (int64_t)(cw + t * 16 + lr) * R + ks * 32 + lk, ks * 32 + lk < R);
+  // bias of the four channels this lane's accumulators hold in each channel tile
+  float bs[kDtWaveT][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) bs[t] = bf2f(bias[cw + t * 16 + lr]);
+  for (int t = 0; t < kDtWaveT; ++t)
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) bs[t][i2] = bf2f(bias[cw + t * 16 + lq * 4 + i2]);
 
-  // dln tile loader: 64 rows x 256 k = 2048 chunks of 16 bytes, 8 per thread; rows past M and k past R
-  // read as zero
+  // dln tile loader: 64 rows x 256 k = 2048 chunks of 16 bytes, 4 per thread.  Rows past M re-read row
+  // M - 1 (their products are never stored) and k past R re-reads column R - 8 (finite values that meet
+  // the zero W_dt fragments), so the loads need no select, which would stall on them at issue.
   typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+  constexpr int kQ = 64 * (kDtMaxR / 8) / kDtStreamThreads;
   auto load_tile = [&](int mt, u32x4* r) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int id = tid + q * 256, row = id >> 5, kc = (id & 31) * 8;
+    for (int q = 0; q < kQ; ++q) {
+      const int id = tid + q * kDtStreamThreads, row = id >> 5, kc = (id & 31) * 8;
       const int m = min(mt * 64 + row, M - 1);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(dln + (int64_t)m * R + min(kc, R - 8));
-      r[q] = (kc < R && mt * 64 + row < M) ? v : u32x4{0u, 0u, 0u, 0u};
+      r[q] = *reinterpret_cast<const u32x4*>(dln + (int64_t)m * R + min(kc, R - 8));
     }
   };
   auto store_tile = [&](int buf, const u32x4* r) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int id = tid + q * 256, row = id >> 5, kc = (id & 31) * 8;
+    for (int q = 0; q < kQ; ++q) {
+      const int id = tid + q * kDtStreamThreads, row = id >> 5, kc = (id & 31) * 8;
       *reinterpret_cast<u32x4*>(&As[buf * 64 * kDtLd + row * kDtLd + kc]) = r[q];
     }
   };
-  u32x4 rt[8];
-  load_tile(mt_beg, rt);
-  store_tile(0, rt);
+  // tile mt_beg goes straight to LDS; tiles mt + 1 and mt + 2 are in flight in registers while tile mt
+  // multiplies, so a load has two tiles' time to land (indices past the range re-read the last tile)
+  u32x4 rt0[kQ], rt1[kQ];
+  load_tile(mt_beg, rt0);
+  store_tile(0, rt0);
+  load_tile(min(mt_beg + 1, mt_end - 1), rt0);
+  load_tile(min(mt_beg + 2, mt_end - 1), rt1);
   __syncthreads();
   int buf = 0;
-  for (int mt = mt_beg; mt < mt_end; ++mt) {
-    load_tile(min(mt + 1, mt_end - 1), rt);          // next tile in flight (the last one re-reads itself)
-    f32x4 acc[4][4];
+  // one tile: multiply LDS[buf], write delta, move the registers' tile into the other buffer and refill
+  // the registers with the tile three ahead
+  auto tile = [&](int mt, u32x4* rg) {
+    f32x4 acc[4][kDtWaveT];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < kDtWaveT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bf16_t* At = As + buf * 64 * kDtLd;
 #pragma unroll
     for (int ks = 0; ks < kDtMaxR / 32; ++ks) {
@@ -266,29 +279,39 @@ __global__ __launch_bounds__(256, 1) void dtproj_mfma_stream_kernel(const bf16_t
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b[ks][t], acc[r][t], 0, 0, 0);
+        for (int t = 0; t < kDtWaveT; ++t)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][t], a[r], acc[r][t], 0, 0, 0);
     }
-    // epilogue: bias + softplus -> bf16 -> this wave's LDS tile -> 16-byte rows.  One wave's LDS accesses
-    // complete in order, so the read-back sees the writes.
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
-          os[(r * 16 + (lane >> 4) * 4 + i2) * kDtOutLd + t * 16 + lr] = f2bf(softplus(acc[r][t][i2] + bs[t]));
+    // epilogue: acc[r][t][i2] is channel t*16 + 4*lq + i2 of token r*16 + lr: bias + softplus, four bf16
+    // channels per 8-byte store
     if (active) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int id = lane + 64 * q, row = id >> 3, cc = (id & 7) * 8;
-        const int m = mt * 64 + row;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&os[row * kDtOutLd + cc]);
-        if (m < M) *reinterpret_cast<u32x4*>(delta + (int64_t)m * C + c0 + cc) = v;
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 64 + r * 16 + lr;
+#pragma unroll
+        for (int t = 0; t < kDtWaveT; ++t) {
+          uint32_t pk[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const uint32_t lo = f2bf(softplus(acc[r][t][2 * h2] + bs[t][2 * h2]));
+            const uint32_t hi = f2bf(softplus(acc[r][t][2 * h2 + 1] + bs[t][2 * h2 + 1]));
+            pk[h2] = lo | (hi << 16);
+          }
+          if (m < M)
+            *reinterpret_cast<uint2*>(delta + (int64_t)m * C + c0 + t * 16 + lq * 4) = make_uint2(pk[0], pk[1]);
+        }
       }
     }
-    store_tile(buf ^ 1, rt);
+    store_tile(buf ^ 1, rg);
+    load_tile(min(mt + 3, mt_end - 1), rg);
     __syncthreads();
     buf ^= 1;
+  };
+  // unrolled by two so the two register sets alternate without copies
+  for (int mt = mt_beg; mt < mt_end; mt += 2) {
+    tile(mt, rt0);
+    if (mt + 1 >= mt_end) break;
+    tile(mt + 1, rt1);
   }
 }
 
@@ -328,7 +351,8 @@ void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, voi
       if (groups > 8) groups = groups / 8 * 8;
       if (groups > nmt) groups = nmt;
       const int per = (nmt + groups - 1) / groups;
-      hipLaunchKernelGGL(dtproj_mfma_stream_kernel, dim3(ncb * groups), dim3(256), 0, st, (const bf16_t*)dln,
+      hipLaunchKernelGGL(dtproj_mfma_stream_kernel, dim3(ncb * groups), dim3(kDtStreamThreads), 0, st,
+                         (const bf16_t*)dln,
                          (const bf16_t*)w, (const bf16_t*)b, (bf16_t*)delta, M, C, R, groups, per);
     } else {
       hipLaunchKernelGGL(dtproj_mfma_kernel, dim3(ncb * nmt), dim3(256), 0, st, (const bf16_t*)dln, (const bf16_t*)w,

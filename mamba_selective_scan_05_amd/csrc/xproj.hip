@@ -27,7 +27,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 constexpr int kMT = 128;         // tokens per workgroup tile
 constexpr int kNG = 288;          // columns per workgroup (18 tiles of 16)
 constexpr int kKB = 64;           // K block staged in LDS
-constexpr int kLd = kKB + 8;      // padded LDS row, bf16 elements
+constexpr int kLd = kKB + 16;     // padded LDS row, bf16 elements (32 bytes of pad: conflict-free 16-byte fragment reads)
 constexpr int kNT = 9;            // 16-wide column tiles per wave
 constexpr int kThreads = 256;
 constexpr int kAChunks = kMT * (kKB / 8) / kThreads;   // 16-byte chunks per thread: 4
