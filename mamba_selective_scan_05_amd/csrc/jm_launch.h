@@ -10,14 +10,16 @@ namespace jm {
 void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
                       const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
 
-// Tokens per x_proj workgroup tile (bf16 path).
+// Tokens per x_proj workgroup tile (bf16 path), and the number of column groups (grid z) for N columns in
+// the wide (288 columns per workgroup) or narrow (32) layout.
 int xproj_token_tile();
+int xproj_column_groups(int N, bool narrow);
 // Most channel slices the x_proj contraction may be split over (the norm step adds at most this many).
 constexpr int kMaxXprojSplits = 16;
 
 // dbc partial sums: part[s, m, n] = sum over channel slice s of xc[m, k] * w[n, k].
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
-                  hipStream_t st);
+                  bool narrow, hipStream_t st);
 
 // Sum the partials in slice order, RMSNorm the dt / B / C slices -> dln [M, R] (io dtype), bc [M, 2N].
 void launch_norm(bool bf16, const float* part, int splits, int M, int R, int N, const void* dt_norm_w,

@@ -28,6 +28,7 @@ struct Plan {
   bool bf16;
   int esize;
   int splits;    // x_proj channel slices
+  bool narrow;   // x_proj in 32-column groups (few tokens)
   int P, Lp;     // scan pieces per sequence, tokens per piece
   int64_t xs, zs;
   int64_t off_xc, off_dbc, off_dln, off_bc, off_delta, off_loc, off_cin, total;
@@ -65,14 +66,24 @@ Plan make_plan(const jm_mixer_dims* d, bool decode) {
   p.xs = d->x_row_stride ? d->x_row_stride : p.C;
   p.zs = d->z_row_stride ? d->z_row_stride : p.C;
 
-  // x_proj split: channel slices of a multiple of 64, dividing C, until the grid is big enough.
+  // x_proj split: channel slices of a multiple of 64, dividing C, until the grid is big enough.  When even
+  // the most slices leave the GPU short of workgroups, the narrow column layout multiplies the grid.
   p.splits = 1;
+  p.narrow = false;
   if (p.bf16) {
     const int64_t tile = jm::xproj_token_tile();
     const int64_t mtiles = (p.T + tile - 1) / tile;
-    while (mtiles * p.splits < kXprojWgTarget && p.splits * 2 <= jm::kMaxXprojSplits &&
-           (p.C / 64) % (p.splits * 2) == 0)
-      p.splits *= 2;
+    auto grow = [&](int64_t groups) {
+      p.splits = 1;
+      while (mtiles * groups * p.splits < kXprojWgTarget && p.splits * 2 <= jm::kMaxXprojSplits &&
+             (p.C / 64) % (p.splits * 2) == 0)
+        p.splits *= 2;
+    };
+    grow(jm::xproj_column_groups(p.W, false));
+    if (mtiles * jm::xproj_column_groups(p.W, false) * p.splits < kXprojWgTarget) {
+      p.narrow = true;
+      grow(jm::xproj_column_groups(p.W, true));
+    }
   }
 
   // scan pieces
@@ -168,7 +179,7 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   marks.mark(0);
   jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st);
   marks.mark(1);
-  jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, st);
+  jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st);
   marks.mark(2);
   jm::launch_norm(p.bf16, dbc, p.splits, (int)p.T, p.R, p.N, w->dt_norm_w, w->b_norm_w, w->c_norm_w,
                   dims->norm_eps, dln, bc, st);

@@ -22,10 +22,11 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kMaxCols = 9;   // ceil((512 + 32) / 64): columns of dbc per lane
-
-template <typename T>
-__global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ part, int splits, int M, int R, int N,
+// norm: one wave per token.  S (the number of x_proj slices) and COLS (columns per lane, 64 columns apart)
+// are compile-time so that every partial-sum load is unconditional (columns past W re-read column W - 1
+// and are dropped): all of a lane's loads are in flight together, then added in slice order.
+template <typename T, int S, int COLS>
+__global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ part, int M, int R, int N,
                                                    const T* __restrict__ wdt, const T* __restrict__ wb,
                                                    const T* __restrict__ wc, float eps, T* __restrict__ dln,
                                                    float* __restrict__ bc) {
@@ -35,19 +36,21 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
   const int W = R + 2 * N;
   const int64_t slice = (int64_t)M * W;
   const float* src = part + (int64_t)m * W;
-  float v[kMaxCols];
+  float pv[COLS][S];
+#pragma unroll
+  for (int i = 0; i < COLS; ++i) {
+    const int col = min(lane + 64 * i, W - 1);
+#pragma unroll
+    for (int p = 0; p < S; ++p) pv[i][p] = src[p * slice + col];
+  }
+  float v[COLS];
   float ss_dt = 0.f, ss_b = 0.f, ss_c = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxCols; ++i) {
+  for (int i = 0; i < COLS; ++i) {
     const int col = lane + 64 * i;
     float s = 0.f;
-    if (col < W) {
-      float pv[kMaxXprojSplits];
 #pragma unroll
-      for (int p = 0; p < kMaxXprojSplits; ++p) pv[p] = p < splits ? src[p * slice + col] : 0.0f;
-#pragma unroll
-      for (int p = 0; p < kMaxXprojSplits; ++p) s += pv[p];
-    }
+    for (int p = 0; p < S; ++p) s += pv[i][p];
     v[i] = s;
     const float sq = s * s;
     if (col < R) ss_dt += sq;
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
   const float r_b = 1.0f / sqrtf(ss_b / N + eps);
   const float r_c = 1.0f / sqrtf(ss_c / N + eps);
 #pragma unroll
-  for (int i = 0; i < kMaxCols; ++i) {
+  for (int i = 0; i < COLS; ++i) {
     const int col = lane + 64 * i;
     if (col < R) {
       io<T>::st(dln + (int64_t)m * R + col, v[i] * r_dt * io<T>::ld(wdt + col));
@@ -71,6 +74,35 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
       bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_c * io<T>::ld(wc + (col - R - N));
     }
   }
+}
+
+template <typename T, int COLS>
+void launch_norm_cols(int splits, dim3 grid, hipStream_t st, const float* part, int M, int R, int N, const T* wdt,
+                      const T* wb, const T* wc, float eps, T* dln, float* bc) {
+  switch (splits) {
+#define JM_NORM_CASE(S)                                                                                       \
+  case S:                                                                                                     \
+    hipLaunchKernelGGL((norm_kernel<T, S, COLS>), grid, dim3(256), 0, st, part, M, R, N, wdt, wb, wc, eps, dln, \
+                       bc);                                                                                   \
+    break;
+    JM_NORM_CASE(1)
+    JM_NORM_CASE(2)
+    JM_NORM_CASE(4)
+    JM_NORM_CASE(8)
+    JM_NORM_CASE(16)
+#undef JM_NORM_CASE
+    default: break;   // the plan only makes power-of-two slice counts up to kMaxXprojSplits
+  }
+}
+
+template <typename T>
+void launch_norm_t(int splits, int M, int R, int N, const T* wdt, const T* wb, const T* wc, float eps, T* dln,
+                   float* bc, const float* part, hipStream_t st) {
+  dim3 grid((M + 3) / 4);
+  if (R + 2 * N <= 5 * 64)
+    launch_norm_cols<T, 5>(splits, grid, st, part, M, R, N, wdt, wb, wc, eps, dln, bc);
+  else
+    launch_norm_cols<T, 9>(splits, grid, st, part, M, R, N, wdt, wb, wc, eps, dln, bc);
 }
 
 constexpr int kDtMaxR = 256;            // dt_rank of the staged bf16 path (larger ranks loop in slices)
@@ -331,13 +363,12 @@ __global__ __launch_bounds__(256) void dtproj_f32_kernel(const float* __restrict
 void launch_norm(bool bf16, const float* part, int splits, int M, int R, int N, const void* wdt, const void* wb,
                  const void* wc, float eps, void* dln, float* bc, hipStream_t st) {
   if (M == 0) return;
-  dim3 grid((M + 3) / 4);
   if (bf16)
-    hipLaunchKernelGGL(norm_kernel<bf16_t>, grid, dim3(256), 0, st, part, splits, M, R, N, (const bf16_t*)wdt,
-                       (const bf16_t*)wb, (const bf16_t*)wc, eps, (bf16_t*)dln, bc);
+    launch_norm_t<bf16_t>(splits, M, R, N, (const bf16_t*)wdt, (const bf16_t*)wb, (const bf16_t*)wc, eps,
+                          (bf16_t*)dln, bc, part, st);
   else
-    hipLaunchKernelGGL(norm_kernel<float>, grid, dim3(256), 0, st, part, splits, M, R, N, (const float*)wdt,
-                       (const float*)wb, (const float*)wc, eps, (float*)dln, bc);
+    launch_norm_t<float>(splits, M, R, N, (const float*)wdt, (const float*)wb, (const float*)wc, eps,
+                         (float*)dln, bc, part, st);
 }
 
 void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, void* delta, int M, int C, int R,

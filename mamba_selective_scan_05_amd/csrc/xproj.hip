@@ -3,7 +3,8 @@
 // bf16 path: matrix cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation.  A workgroup of 4 waves owns a
 // 128-token x 288-column output tile: wave (mg, ng) computes rows [64 mg, 64 mg + 64) x 16-wide column
 // tiles [9 ng, 9 ng + 9), so every xc element is read from HBM once and every W_x element once per
-// 128 tokens.  Both operands of each 64-wide K block are staged through LDS (double-buffered, rows
+// 128 tokens.  With few tokens (decode) the workgroups take 32-column groups instead (one tile per wave),
+// which multiplies the grid by 9 without adding partial sums; xc is then re-read from L2 per group.  Both operands of each 64-wide K block are staged through LDS (double-buffered, rows
 // padded by 16 bytes against bank conflicts); the next block's global loads are in flight while the
 // current block's MFMAs run.  When there are too few token tiles to fill the GPU, the K range is split
 // over `splits` workgroups that write fp32 partial sums (added in a fixed order by the norm step, so the
@@ -25,23 +26,26 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
 constexpr int kMT = 128;         // tokens per workgroup tile
-constexpr int kNG = 288;          // columns per workgroup (18 tiles of 16)
 constexpr int kKB = 64;           // K block staged in LDS
 constexpr int kLd = kKB + 16;     // padded LDS row, bf16 elements (32 bytes of pad: conflict-free 16-byte fragment reads)
-constexpr int kNT = 9;            // 16-wide column tiles per wave
 constexpr int kThreads = 256;
 constexpr int kAChunks = kMT * (kKB / 8) / kThreads;   // 16-byte chunks per thread: 4
-constexpr int kBChunks = kNG * (kKB / 8) / kThreads;   // 9
+// Column tiles per wave: 9 (a workgroup covers 288 columns) normally; 1 (32 columns, grid z walks the
+// column groups) when there are too few token tiles to fill the GPU even with the K range split.
+constexpr int kNTWide = 9, kNTNarrow = 1;
 
 __device__ __forceinline__ bf16x8 lds_frag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // MFMA 16x16x32 operand layout used here: lane l supplies row (l % 16) of A and column (l % 16) of B,
 // both over the 8 consecutive k values 8*(l / 16) .. +7 (the same k set for A and B, so the product is
 // independent of how the hardware orders k).  The accumulator holds rows 4*(l / 16) + i, column l % 16.
+template <int kNT>
 __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __restrict__ xc,
                                                               const bf16_t* __restrict__ w,
                                                               float* __restrict__ part, int M, int N, int K,
                                                               int splits) {
+  constexpr int kNG = 32 * kNT;                               // columns per workgroup
+  constexpr int kBChunks = kNG * (kKB / 8) / kThreads;        // 16-byte W_x chunks per thread
   __shared__ __attribute__((aligned(16))) bf16_t As[2][kMT * kLd];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kNG * kLd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -183,13 +187,22 @@ __global__ __launch_bounds__(64) void xproj_f32_kernel(const float* __restrict__
 
 int xproj_token_tile() { return kMT; }
 
+int xproj_column_groups(int N, bool narrow) {
+  const int cols = 32 * (narrow ? kNTNarrow : kNTWide);
+  return (N + cols - 1) / cols;
+}
+
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
-                  hipStream_t st) {
+                  bool narrow, hipStream_t st) {
   if (M == 0) return;
   if (bf16) {
-    dim3 grid(((M + kMT - 1) / kMT) * splits, 1, (N + kNG - 1) / kNG);
-    hipLaunchKernelGGL(xproj_mfma_kernel, grid, dim3(kThreads), 0, st, (const bf16_t*)xc, (const bf16_t*)w, part,
-                       M, N, K, splits);
+    dim3 grid(((M + kMT - 1) / kMT) * splits, 1, xproj_column_groups(N, narrow));
+    if (narrow)
+      hipLaunchKernelGGL(xproj_mfma_kernel<kNTNarrow>, grid, dim3(kThreads), 0, st, (const bf16_t*)xc,
+                         (const bf16_t*)w, part, M, N, K, splits);
+    else
+      hipLaunchKernelGGL(xproj_mfma_kernel<kNTWide>, grid, dim3(kThreads), 0, st, (const bf16_t*)xc,
+                         (const bf16_t*)w, part, M, N, K, splits);
   } else {
     dim3 grid(M, (N + 63) / 64);
     hipLaunchKernelGGL(xproj_f32_kernel, grid, dim3(64), 0, st, (const float*)xc, (const float*)w, part, M, N, K);
