@@ -144,6 +144,54 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T* __restrict__ x,
   }
 }
 
+// One token per sequence (decode): each thread takes 16 bytes of channels, reads their old conv state and
+// the new input, writes xc and the shifted conv state.  The thread reads the state before writing it, so
+// conv_out may alias conv_in.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x, int64_t xs,
+                                                        const T* __restrict__ conv_w, const T* __restrict__ conv_b,
+                                                        const T* conv_in, T* __restrict__ xc, T* conv_out, int C) {
+  constexpr int V = Vec16<T>::n;
+  const int c0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
+  if (c0 >= C) return;
+  const int b = blockIdx.y;
+  float st[(kTaps - 1) * V], cur[V], wf[V * kTaps], bias[V];
+  const int64_t so = ((int64_t)b * C + c0) * (kTaps - 1);
+  if (conv_in) {
+#pragma unroll
+    for (int q = 0; q < kTaps - 1; ++q) load16(conv_in + so + q * V, st + q * V);
+  } else {
+#pragma unroll
+    for (int i = 0; i < (kTaps - 1) * V; ++i) st[i] = 0.0f;
+  }
+  load16(x + (int64_t)b * xs + c0, cur);
+#pragma unroll
+  for (int q = 0; q < V * kTaps; q += V) load16(conv_w + (int64_t)c0 * kTaps + q, wf + q);
+  if (conv_b) {
+    load16(conv_b + c0, bias);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) bias[i] = 0.0f;
+  }
+  float o[V], ns[(kTaps - 1) * V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const float* s3 = st + i * (kTaps - 1);
+    float u = bias[i];
+    u = fmaf(wf[i * kTaps + 0], s3[0], u);
+    u = fmaf(wf[i * kTaps + 1], s3[1], u);
+    u = fmaf(wf[i * kTaps + 2], s3[2], u);
+    u = fmaf(wf[i * kTaps + 3], cur[i], u);
+    o[i] = silu(u);
+    ns[i * (kTaps - 1) + 0] = s3[1];
+    ns[i * (kTaps - 1) + 1] = s3[2];
+    ns[i * (kTaps - 1) + 2] = cur[i];
+  }
+  store16(xc + (int64_t)b * C + c0, o);
+#pragma unroll
+  for (int q = 0; q < kTaps - 1; ++q) store16(conv_out + so + q * V, ns + q * V);
+}
+
 template <typename T>
 __global__ void state_passthrough_kernel(const T* __restrict__ conv_in, T* __restrict__ conv_out,
                                          const float* __restrict__ h0, float* __restrict__ h_out, int B, int C) {
@@ -174,6 +222,19 @@ void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, 
   else
     hipLaunchKernelGGL(conv_silu_kernel<float>, grid, block, 0, st, (const float*)x, xs, (const float*)conv_w,
                        (const float*)conv_b, (const float*)conv_in, (float*)xc, L, C, run);
+}
+
+void launch_conv_step(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
+                      const void* conv_in, void* xc, void* conv_out, int B, int C, hipStream_t st) {
+  const int V = bf16 ? 8 : 4;
+  dim3 grid((C / V + 255) / 256, B);
+  if (bf16)
+    hipLaunchKernelGGL(conv_step_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, xs,
+                       (const bf16_t*)conv_w, (const bf16_t*)conv_b, (const bf16_t*)conv_in, (bf16_t*)xc,
+                       (bf16_t*)conv_out, C);
+  else
+    hipLaunchKernelGGL(conv_step_kernel<float>, grid, dim3(256), 0, st, (const float*)x, xs, (const float*)conv_w,
+                       (const float*)conv_b, (const float*)conv_in, (float*)xc, (float*)conv_out, C);
 }
 
 void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,

@@ -10,6 +10,11 @@ namespace jm {
 void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
                       const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
 
+// One token per sequence (seqlen 1): the same conv + SiLU -> xc [B, C], and the shifted conv state ->
+// conv_state_out [B, C, K-1] (may alias conv_state_in; zeros stand in for a NULL conv_state_in).
+void launch_conv_step(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
+                      const void* conv_state_in, void* xc, void* conv_state_out, int B, int C, hipStream_t st);
+
 // Tokens per x_proj workgroup tile (bf16 path), and the number of column groups (grid z) for N columns in
 // the wide (288 columns per workgroup) or narrow (32) layout.
 int xproj_token_tile();
@@ -43,7 +48,7 @@ struct ScanArgs {
   const void* x;         // raw input, for the conv state
   int64_t x_stride;
   const void* conv_in;   // [B, C, K-1] or null
-  void* conv_out;        // [B, C, K-1]
+  void* conv_out;        // [B, C, K-1], or null when the conv step already wrote the state
   float* loc;            // [B, P, N+1, C]   per-piece local end states and dt sums (P > 1)
   float* cin;            // [B, P, N, C]     per-piece incoming states (P > 1)
   int B, L, C, P, Lp;

@@ -177,7 +177,12 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   void* delta = base + p.off_delta;
 
   marks.mark(0);
-  jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st);
+  // one token per sequence: the single-step conv also writes the conv state, so the scan skips it
+  const bool step = p.L == 1;
+  if (step)
+    jm::launch_conv_step(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, conv_out, p.B, p.C, st);
+  else
+    jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st);
   marks.mark(1);
   jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st);
   marks.mark(2);
@@ -199,7 +204,7 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.x = x;
   a.x_stride = p.xs;
   a.conv_in = conv_in;
-  a.conv_out = conv_out;
+  a.conv_out = step ? nullptr : conv_out;
   a.loc = p.P > 1 ? (float*)(base + p.off_loc) : nullptr;
   a.cin = p.P > 1 ? (float*)(base + p.off_cin) : nullptr;
   a.B = p.B;

@@ -215,8 +215,9 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     float* ho = a.h_out + ((int64_t)b * C + c) * kN;
 #pragma unroll
     for (int n = 0; n < kN; ++n) ho[n] = h[n];
-    // conv state: the last K-1 entries of the extended input (old state entries when L < K-1).  All three
-    // are read before any is written, so conv_out may alias conv_in.
+    // conv state (unless the conv step wrote it): the last K-1 entries of the extended input (old state
+    // entries when L < K-1).  All three are read before any is written, so conv_out may alias conv_in.
+    if (!a.conv_out) return;
     const T* x = (const T*)a.x;
     const T* ci = (const T*)a.conv_in;
     T v[kTaps - 1];
