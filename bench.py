@@ -29,6 +29,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+# fp32 vector ALU: 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T lane-operations/s (AMD's published
+# 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops).  Transcendentals (exp, rcp) issue at a quarter
+# of that rate, so each is counted as TRANS_SLOTS full-rate operations.
+VALU_PEAK_TOPS = 78.6
+TRANS_SLOTS = 4
 N_STATE_SETS = 4               # decode state sets rotated per step (4 x 140 MB > the 256 MB last-level cache)
 
 
@@ -78,6 +83,17 @@ def algorithmic_bytes(B, L, C, N, R, esize):
         "norm_dt_proj": T * W * 4 + T * C * esize + T * 2 * N * 4 + C * R * esize + C * esize,
         "scan_gate": T * C * 4 * esize + T * 2 * N * 4 + 2 * B * C * N * 4 + C * (N + 1) * esize,
     }
+
+
+def scan_alu_ops(B, L, C, N):
+    """fp32 VALU work of the scan + gate as the recurrence defines it, one sequential pass over the tokens, in
+    full-rate issue slots.  Per (token, channel, state): delta*A, its exponential, (delta*x)*B, the state FMA
+    and the C.h FMA = 4 operations + 1 transcendental.  Per (token, channel): delta*x, the D*x FMA, y*SiLU(z)
+    and SiLU's multiply, add and multiply = 6 operations + 2 transcendentals (exp, reciprocal)."""
+    tc = B * L * C
+    ops = tc * N * 4 + tc * 6
+    trans = tc * N + tc * 2
+    return ops + TRANS_SLOTS * trans
 
 
 def decode_bytes(B, C, N, R, K, esize):
@@ -336,7 +352,20 @@ def main():
     for k, t in pre["stage_ms"].items():
         log(f"  {k:12s} {t * 1e3:9.2f} us")
     dom = max(groups, key=lambda k: groups[k])
-    ach = stages[dom]["GB_s"]
+    if dom == "scan_gate":
+        # the scan is bound by the vector ALU (16 exponentials per token and channel), not by HBM
+        ops = scan_alu_ops(B, L, C, N)
+        ach = ops / (groups[dom] * 1e-3) / 1e12
+        roofline = {"bound": "alu", "kernel": dom, "achieved": round(ach, 2), "peak": VALU_PEAK_TOPS,
+                    "unit": "T fp32 lane-ops/s (transcendental = 4)", "frac": round(ach / VALU_PEAK_TOPS, 4),
+                    "traffic": measured_traffic(cfg.name, dom), "alg_ops_per_launch": ops,
+                    "alg_bytes_per_launch": alg[dom], "hbm_GB_s": stages[dom]["GB_s"],
+                    "us_per_launch": stages[dom]["us"]}
+    else:
+        ach = stages[dom]["GB_s"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
+                    "alg_bytes_per_launch": alg[dom], "us_per_launch": stages[dom]["us"]}
     xflops = 2.0 * tokens * (R + 2 * N) * C
     stages["x_proj"]["mfma_tflops"] = round(xflops / (groups["x_proj"] * 1e-3) / 1e12, 2)
     stages["x_proj"]["frac_mfma_bf16"] = round(stages["x_proj"]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
@@ -356,9 +385,7 @@ def main():
         "config": {"workload": f"{cfg.name}: Jamba-v0.1 Mamba mixer prefill", "batch": B, "seq_len": L,
                    "d_inner": C, "d_state": N, "dt_rank": R, "d_conv": cfg.d_conv, "io": "bf16",
                    "state": "fp32", "x_proj_splits": pre["splits"], "scan_pieces": pre["pieces"]},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
-                     "alg_bytes_per_launch": alg[dom], "us_per_launch": stages[dom]["us"]},
+        "roofline": roofline,
         "stages": stages,
         "mixer_GB_s": round(sum(alg.values()) / (pre["ms"] * 1e-3) / 1e9, 1),
     }

@@ -6,12 +6,10 @@
 // The normalised dt goes out in the I/O dtype (it is the next contraction's operand), B and C in fp32.
 //
 // dt_proj: delta[m, c] = softplus(sum_r dln[m, r] * W[c, r] + b[c]).  bf16 path on matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation): a workgroup of 4 waves computes a 64-token x 256-channel
-// tile, each wave 64 x 64.  The dln tile is staged once in LDS for the 4 waves; each wave issues all its
-// W_dt fragment loads up front.  Bias and softplus are fused into the epilogue, which transposes the tile
-// through LDS so that delta rows leave in 16-byte stores.  Workgroups are mapped so that each XCD walks
-// the token tiles of a fixed set of channel blocks, keeping those W_dt rows in its L2.  fp32 path on the
-// vector ALU.
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation): for dt_rank <= 256 persistent 8-wave workgroups keep W_dt in
+// registers and stream 64-token dln tiles (dtproj_mfma_stream_kernel); larger ranks take a tiled kernel in
+// which a workgroup of 4 waves computes a 64-token x 256-channel tile and transposes it through LDS for
+// 16-byte stores.  Bias and softplus are fused into both epilogues.  fp32 path on the vector ALU.
 #include "jm_device.h"
 #include "jm_launch.h"
 

@@ -7,7 +7,7 @@
 // One lane owns one channel of one sequence and keeps its 16-wide fp32 state in registers; B_t and C_t
 // are shared by every channel, so a wave reads them as wave-uniform (scalar) loads.  exp(delta * A) is
 // evaluated as 2^(delta * A * log2 e) with A * log2 e precomputed per state.  Tokens are processed in
-// batches of 8 whose per-channel loads (delta, xc, z) are issued one batch ahead, so HBM latency hides
+// batches of 4 whose per-channel loads (delta, xc, z) are issued one batch ahead, so HBM latency hides
 // behind the arithmetic of the current batch.  The kernel is bound by the vector ALU (16 exponentials
 // and about 64 other operations per token and channel), not by HBM.
 //

@@ -4,8 +4,9 @@
 // 128-token x 288-column output tile: wave (mg, ng) computes rows [64 mg, 64 mg + 64) x 16-wide column
 // tiles [9 ng, 9 ng + 9), so every xc element is read from HBM once and every W_x element once per
 // 128 tokens.  With few tokens (decode) the workgroups take 32-column groups instead (one tile per wave),
-// which multiplies the grid by 9 without adding partial sums; xc is then re-read from L2 per group.  Both operands of each 64-wide K block are staged through LDS (double-buffered, rows
-// padded by 16 bytes against bank conflicts); the next block's global loads are in flight while the
+// which multiplies the grid by 9 without adding partial sums; xc is then re-read from L2 per group.  Both
+// operands of each 64-wide K block are staged through LDS (double-buffered, rows padded by 32 bytes against
+// bank conflicts); the next block's global loads are in flight while the
 // current block's MFMAs run.  When there are too few token tiles to fill the GPU, the K range is split
 // over `splits` workgroups that write fp32 partial sums (added in a fixed order by the norm step, so the
 // result is deterministic).  Split s of token tile t runs as workgroup t * splits + s: workgroups are
