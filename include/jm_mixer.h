@@ -162,6 +162,9 @@ typedef struct jm_workspace_layout {
   int32_t dbc_splits;     /* number of channel slices the x_proj contraction is split over */
   int32_t scan_chunks;    /* number of sequence pieces the scan runs in parallel per channel */
   int64_t total_bytes;
+  int32_t xproj_path;     /* x_proj kernel layout: 0: bf16 matrix cores, 288-column tiles; 1: bf16 matrix
+                             cores, 32-column groups (few tokens); 2: fp32 on the vector ALU */
+  int32_t reserved;
 } jm_workspace_layout;
 
 int jm_mixer_prefill_workspace_layout(const jm_mixer_dims* dims, jm_workspace_layout* layout);

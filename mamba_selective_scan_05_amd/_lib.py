@@ -45,7 +45,8 @@ class Weights(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("xc", ctypes.c_int64), ("dbc", ctypes.c_int64), ("dln", ctypes.c_int64), ("bc", ctypes.c_int64),
                 ("delta", ctypes.c_int64), ("carries", ctypes.c_int64), ("dbc_splits", ctypes.c_int32),
-                ("scan_chunks", ctypes.c_int32), ("total_bytes", ctypes.c_int64)]
+                ("scan_chunks", ctypes.c_int32), ("total_bytes", ctypes.c_int64), ("xproj_path", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None

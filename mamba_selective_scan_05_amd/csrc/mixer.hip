@@ -280,6 +280,8 @@ int jm_mixer_prefill_workspace_layout(const jm_mixer_dims* dims, jm_workspace_la
   layout->dbc_splits = p.splits;
   layout->scan_chunks = p.P;
   layout->total_bytes = p.total;
+  layout->xproj_path = !p.bf16 ? 2 : p.narrow ? 1 : 0;
+  layout->reserved = 0;
   return JM_OK;
 }
 

@@ -4,14 +4,13 @@
 // 128-token x 288-column output tile: wave (mg, ng) computes rows [64 mg, 64 mg + 64) x 16-wide column
 // tiles [9 ng, 9 ng + 9), so every xc element is read from HBM once and every W_x element once per
 // 128 tokens.  With few tokens (decode) the workgroups take 32-column groups instead (one tile per wave),
-// which multiplies the grid by 9 without adding partial sums; xc is then re-read from L2 per group.  Both
-// operands of each 64-wide K block are staged through LDS (double-buffered, rows padded by 32 bytes against
-// bank conflicts); the next block's global loads are in flight while the
-// current block's MFMAs run.  When there are too few token tiles to fill the GPU, the K range is split
-// over `splits` workgroups that write fp32 partial sums (added in a fixed order by the norm step, so the
-// result is deterministic).  Split s of token tile t runs as workgroup t * splits + s: workgroups are
-// handed to the 8 XCDs round-robin, so each XCD works on a fixed subset of K slices and keeps their
-// W_x rows in its own L2.  Wider projections (N > 288) run as several column groups (grid z).
+// which multiplies the grid by 9 without adding partial sums; xc is then re-read from L2 per group.  The
+// operands of each 64-wide K block reach LDS by direct global-to-LDS loads in a three-stage pipeline (see
+// below).  When there are too few token tiles to fill the GPU, the K range is split over `splits`
+// workgroups that write fp32 partial sums (added in a fixed order by the norm step, so the result is
+// deterministic).  Split s of token tile t runs as workgroup t * splits + s: workgroups are handed to the
+// 8 XCDs round-robin, so each XCD works on a fixed subset of K slices and keeps their W_x rows in its own
+// L2.  Wider projections (N > 288) run as several column groups (grid z).
 //
 // fp32 path: plain fp32 dot products on the vector ALU (the fp32 I/O mode must not round xc to bf16).
 #include "jm_device.h"
@@ -23,14 +22,10 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-// 16 bytes in registers as a native vector (HIP's uint4 class does not always stay in registers when copied)
-typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
 constexpr int kMT = 128;         // tokens per workgroup tile
-constexpr int kKB = 64;           // K block staged in LDS
-constexpr int kLd = kKB + 16;     // padded LDS row, bf16 elements (32 bytes of pad: conflict-free 16-byte fragment reads)
+constexpr int kKB = 64;           // K block staged in LDS (one 128-byte LDS row per token / column)
 constexpr int kThreads = 256;
-constexpr int kAChunks = kMT * (kKB / 8) / kThreads;   // 16-byte chunks per thread: 4
 // Column tiles per wave: 9 (a workgroup covers 288 columns) normally; 1 (32 columns, grid z walks the
 // column groups) when there are too few token tiles to fill the GPU even with the K range split.
 constexpr int kNTWide = 9, kNTNarrow = 1;
@@ -40,15 +35,38 @@ __device__ __forceinline__ bf16x8 lds_frag(const bf16_t* p) { return *reinterpre
 // MFMA 16x16x32 operand layout used here: lane l supplies row (l % 16) of A and column (l % 16) of B,
 // both over the 8 consecutive k values 8*(l / 16) .. +7 (the same k set for A and B, so the product is
 // independent of how the hardware orders k).  The accumulator holds rows 4*(l / 16) + i, column l % 16.
+//
+// Operands reach LDS by direct global-to-LDS loads (16 bytes per lane, lane i of an instruction lands at
+// byte 16 i of its destination), three K blocks deep: while block b multiplies, blocks b + 1 and b + 2 are
+// in flight, with no staging registers.  LDS rows are 128 bytes (64 k) with no padding; 16-byte chunk j of
+// row r sits in slot j ^ (r & 7), which makes the fragment reads conflict-free (measured: 12 conflict cycles
+// per read without the swizzle, none with it).  A lane loads whichever global chunk belongs in its slot.
+constexpr int kStages = 3;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+__device__ __forceinline__ int swz(int r, int j) { return r * kKB + ((j ^ (r & 7)) << 3); }
+// Workgroup barrier without __syncthreads' release fence: that fence would wait for every direct-to-LDS
+// load in flight (they count as LDS writes).  Each wave has already waited for the loads of the block it
+// hands over; the asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt operand (gfx9 encoding): vector-memory count n, the other counters at their maxima
+__device__ __forceinline__ constexpr int wait_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
+
 template <int kNT>
 __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __restrict__ xc,
                                                               const bf16_t* __restrict__ w,
                                                               float* __restrict__ part, int M, int N, int K,
                                                               int splits) {
   constexpr int kNG = 32 * kNT;                               // columns per workgroup
-  constexpr int kBChunks = kNG * (kKB / 8) / kThreads;        // 16-byte W_x chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][kMT * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kNG * kLd];
+  constexpr int kAL = kMT / 8 / 4;                            // direct loads per wave per block: A rows / 8 / waves
+  constexpr int kBL = kNG / 8 / 4;
+  // one array per stage, so the compiler can tell the loads in flight into one stage from reads of another
+  __shared__ __attribute__((aligned(16))) bf16_t As0[kMT * kKB], As1[kMT * kKB], As2[kMT * kKB];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs0[kNG * kKB], Bs1[kNG * kKB], Bs2[kNG * kKB];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int s = blockIdx.x % splits;
   const int m0 = (blockIdx.x / splits) * kMT;
@@ -56,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __re
   const int kps = K / splits;
   const int kbeg = s * kps;
   const int nblocks = kps / kKB;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int lr = lane & 15, lk = lane >> 4;
   const int mg = wave & 1, ng = wave >> 1;
 
   f32x4 acc[4][kNT];
@@ -65,91 +83,67 @@ __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __re
 #pragma unroll
     for (int t = 0; t < kNT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // xc (from HBM) is loaded two K blocks ahead, W_x (from L2) one block ahead.  Rows past M (tokens) or
-  // N (columns) are clamped to the last valid row: they only feed outputs that are never stored, and
-  // branch-free loads let the memory counter be waited on precisely.
-  // Per-thread chunk addresses: chunk q of a block is row (tid + q * 256) / 8, k offset ((tid + q*256) % 8)*8.
-  const int kc = (tid & 7) * 8;
-  const bf16_t* pa[kAChunks];
-  const bf16_t* pb[kBChunks];
-  int la[kAChunks], lb[kBChunks];
+  // Load q of this wave fills LDS rows 8 (wave * count + q) .. + 7; lane l takes row + l / 8, slot l % 8, so
+  // it reads the global chunk (l % 8) ^ (row & 7).  Rows past M (tokens) or N (columns) re-read the last
+  // valid row: they only feed outputs that are never stored.
+  const bf16_t* pa[kAL];
+  const bf16_t* pb[kBL];
 #pragma unroll
-  for (int q = 0; q < kAChunks; ++q) {
-    const int row = (tid >> 3) + q * (kThreads / 8);
-    pa[q] = xc + (int64_t)min(m0 + row, M - 1) * K + kc;
-    la[q] = row * kLd + kc;
+  for (int q = 0; q < kAL; ++q) {
+    const int row = (wave * kAL + q) * 8 + (lane >> 3);
+    pa[q] = xc + (int64_t)min(m0 + row, M - 1) * K + (((lane & 7) ^ (row & 7)) << 3);
   }
 #pragma unroll
-  for (int q = 0; q < kBChunks; ++q) {
-    const int row = (tid >> 3) + q * (kThreads / 8);
-    pb[q] = w + (int64_t)min(n0 + row, N - 1) * K + kc;
-    lb[q] = row * kLd + kc;
+  for (int q = 0; q < kBL; ++q) {
+    const int row = (wave * kBL + q) * 8 + (lane >> 3);
+    pb[q] = w + (int64_t)min(n0 + row, N - 1) * K + (((lane & 7) ^ (row & 7)) << 3);
   }
-  // K blocks go in pairs (even block from LDS buffer 0, odd from buffer 1) with two register sets for xc
-  // (X, Y), so a prefetched block never has to be copied between registers.  While block b computes:
-  // W_x of b + 1 and xc of b + 2 are requested (W_x first: the memory counter drains in issue order, so
-  // the LDS store at the end of the block waits for W_x and the older xc only); afterwards xc of b + 1
-  // (already in registers) and W_x of b + 1 go to the other LDS buffer.  Loads past the last block re-read
-  // it, and the LDS stores are unconditional (the last one fills the idle buffer): conditional loads or
-  // stores would let the compiler sink the loads past the MFMAs.
-  u32x4 rx[kAChunks], ry[kAChunks], rb[kBChunks];
-  auto blk = [&](int b) { return kbeg + min(b, nblocks - 1) * kKB; };
+  // block b (past the last one: the last again, into a stage nobody reads) -> stage (A, B)
+  auto issue = [&](int b, bf16_t* A, bf16_t* B) {
+    const int kb = kbeg + min(b, nblocks - 1) * kKB;
 #pragma unroll
-  for (int q = 0; q < kAChunks; ++q) ry[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(0));
+    for (int q = 0; q < kAL; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(pa[q] + kb), (lds_void_t*)(A + (wave * kAL + q) * 8 * kKB),
+                                       16, 0, 0);
 #pragma unroll
-  for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const u32x4*>(pb[q] + blk(0));
+    for (int q = 0; q < kBL; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(pb[q] + kb), (lds_void_t*)(B + (wave * kBL + q) * 8 * kKB),
+                                       16, 0, 0);
+  };
+  auto compute = [&](const bf16_t* A, const bf16_t* B) {
 #pragma unroll
-  for (int q = 0; q < kAChunks; ++q) rx[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(1));
-#pragma unroll
-  for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<u32x4*>(&As[0][la[q]]) = ry[q];
-#pragma unroll
-  for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<u32x4*>(&Bs[0][lb[q]]) = rb[q];
-  __syncthreads();
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < kKB; ks += 32) {
+    for (int ks = 0; ks < kKB / 8; ks += 4) {
       bf16x8 a[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = lds_frag(&As[buf][(mg * 64 + r * 16 + lr) * kLd + ks + lk]);
+      for (int r = 0; r < 4; ++r) a[r] = lds_frag(&A[swz(mg * 64 + r * 16 + lr, ks + lk)]);
 #pragma unroll
       for (int t = 0; t < kNT; ++t) {
-        const bf16x8 bv = lds_frag(&Bs[buf][((ng * kNT + t) * 16 + lr) * kLd + ks + lk]);
+        const bf16x8 bv = lds_frag(&B[swz((ng * kNT + t) * 16 + lr, ks + lk)]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bv, acc[r][t], 0, 0, 0);
       }
     }
   };
-
-  for (int ib = 0; ib < nblocks; ib += 2) {
-    // even block ib (buffer 0); rx holds xc of ib + 1
-#pragma unroll
-    for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const u32x4*>(pb[q] + blk(ib + 1));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < kAChunks; ++q) ry[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(ib + 2));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-#pragma unroll
-    for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<u32x4*>(&As[1][la[q]]) = rx[q];
-#pragma unroll
-    for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<u32x4*>(&Bs[1][lb[q]]) = rb[q];
-    __syncthreads();
-    if (ib + 1 >= nblocks) break;
-    // odd block ib + 1 (buffer 1); ry holds xc of ib + 2
-#pragma unroll
-    for (int q = 0; q < kBChunks; ++q) rb[q] = *reinterpret_cast<const u32x4*>(pb[q] + blk(ib + 2));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < kAChunks; ++q) rx[q] = *reinterpret_cast<const u32x4*>(pa[q] + blk(ib + 3));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-#pragma unroll
-    for (int q = 0; q < kAChunks; ++q) *reinterpret_cast<u32x4*>(&As[0][la[q]]) = ry[q];
-#pragma unroll
-    for (int q = 0; q < kBChunks; ++q) *reinterpret_cast<u32x4*>(&Bs[0][lb[q]]) = rb[q];
-    __syncthreads();
+  // Block b: wait until this thread's loads of block b have landed (block b + 1's may still be in flight),
+  // then a barrier (everyone's have, and everyone is done with block b - 1), then refill block b - 1's
+  // stage with block b + 2 and multiply block b.  Unrolled by three so every stage index is a constant.
+  issue(0, As0, Bs0);
+  issue(1, As1, Bs1);
+  auto step = [&](int b, const bf16_t* A, const bf16_t* B, bf16_t* An, bf16_t* Bn) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(kAL + kBL));
+    stage_barrier();
+    issue(b + 2, An, Bn);
+    compute(A, B);
+  };
+  for (int b = 0;; b += 3) {
+    step(b, As0, Bs0, As2, Bs2);
+    if (b + 1 >= nblocks) break;
+    step(b + 1, As1, Bs1, As0, Bs0);
+    if (b + 2 >= nblocks) break;
+    step(b + 2, As2, Bs2, As1, Bs1);
+    if (b + 3 >= nblocks) break;
   }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));   // the surplus loads must land before the workgroup's LDS is reused
 
   float* dst = part + (int64_t)s * M * N;
 #pragma unroll

@@ -84,6 +84,16 @@ def test_bf16_wide_strided_views():
     _run_and_check(cfg, row_stride=2 * 512 + 64)
 
 
+@pytest.mark.parametrize("with_state", [True, False])
+def test_bf16_wide_xproj_tiles_across_sequences(with_state):
+    # enough tokens for x_proj's 288-column tiles (its three-stage LDS pipeline): sequence starts fall inside
+    # 128-token tiles, a ragged last tile, strided x and z, with and without incoming states
+    import mamba_selective_scan_05_amd as jm
+    cfg = _small(f"wide_xproj_{'state' if with_state else 'nostate'}", 3, 2900, 256, 16, "bf16", 21)
+    assert jm.workspace_layout(jm.make_dims(3, 2900, 256, 16, jm.JM_BF16)).xproj_path == 0
+    _run_and_check(cfg, with_state=with_state, row_stride=528)
+
+
 @pytest.mark.parametrize("L", [0, 1, 2, 3, 5, 64, 65])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_short_sequences_and_conv_state(L, io):
