@@ -223,15 +223,22 @@ __global__ __launch_bounds__(256, 2) void dtproj_mfma_kernel(const bf16_t* __res
 
 // dt_rank <= 256: persistent workgroups of 8 waves (two per SIMD).  Each wave holds the W_dt rows of its 32
 // channels for the whole K (dt_rank) in registers and walks a contiguous range of 64-token tiles; the dln
-// tiles stream through double-buffered LDS (the next tile's loads are in flight while the current one
-// multiplies).  W_dt is the A operand and the dln tile the B operand, so a lane's accumulator holds four
-// consecutive channels of one token and leaves as one 8-byte store, with no transpose.  Workgroup i runs
-// on XCD i % 8 and takes token-tile group i % G, so each XCD keeps its group's dln tiles in its L2.
+// tiles stream through double-buffered LDS with the next two tiles in flight in registers.  W_dt is the A
+// operand and the dln tile the B operand, so a lane's accumulator holds four consecutive channels of one
+// token.  The waves are software-pipelined: the MFMAs of tile t + 1 (into a second set of accumulators) are
+// interleaved with the bias + softplus of tile t, so the matrix cores and the vector ALU work at the same
+// time.  The softplus results go to a double-buffered LDS tile (64 tokens x 256 channels) and, after the next
+// barrier, the workgroup writes them as whole 512-byte delta rows with 16-byte lanes: one store instruction
+// then covers 8 full cache lines instead of 16 partial ones (the memory pipeline, not the math, bounded the
+// kernel with per-lane 8-byte stores).  Stores go through a per-tile buffer resource whose range ends at the
+// last token, so there are no branches.  Workgroup i runs on XCD i % 8 and takes token-tile group i % G, so
+// each XCD keeps its group's dln tiles in its L2.
 constexpr int kDtStreamWaves = 8;
 constexpr int kDtStreamThreads = 64 * kDtStreamWaves;
 constexpr int kDtWaveCh = 256 / kDtStreamWaves;         // channels per wave
 constexpr int kDtWaveT = kDtWaveCh / 16;                 // 16-channel MFMA tiles per wave
-constexpr int kDtLdsA = 2 * 64 * kDtLd * 2;              // two dln tiles (bytes)
+constexpr int kDtBufferFlags = 0x00020000;               // dword 3 of a raw buffer descriptor on gfx9-family GPUs
+constexpr int kDtStreamOutLd = 256 + 8;                  // padded row of the LDS output tile (bf16)
 __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel(const bf16_t* __restrict__ dln,
                                                                                const bf16_t* __restrict__ w,
                                                                                const bf16_t* __restrict__ bias,
@@ -239,12 +246,14 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
                                                                                int C, int R, int groups,
                                                                                int tiles_per_group) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2 * 64 * kDtLd];
+  __shared__ __attribute__((aligned(16))) bf16_t Os[2 * 64 * kDtStreamOutLd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
   const int nmt = (M + 63) / 64;
   const int g = blockIdx.x % groups, cb = blockIdx.x / groups;
   const int mt_beg = g * tiles_per_group, mt_end = min(nmt, mt_beg + tiles_per_group);
   if (mt_beg >= mt_end) return;                      // uniform over the workgroup
+  const int ntiles = mt_end - mt_beg;
   const int c0 = cb * 256 + wave * kDtWaveCh;
   const bool active = c0 < C;
   const int cw = active ? c0 : 0;                    // waves past C read valid rows and store nothing
@@ -265,10 +274,12 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
 
   // dln tile loader: 64 rows x 256 k = 2048 chunks of 16 bytes, 4 per thread.  Rows past M re-read row
   // M - 1 (their products are never stored) and k past R re-reads column R - 8 (finite values that meet
-  // the zero W_dt fragments), so the loads need no select, which would stall on them at issue.
+  // the zero W_dt fragments), so the loads need no select, which would stall on them at issue.  Tiles past
+  // the group re-read its last tile.
   typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
   constexpr int kQ = 64 * (kDtMaxR / 8) / kDtStreamThreads;
-  auto load_tile = [&](int mt, u32x4* r) {
+  auto load_tile = [&](int i, u32x4* r) {
+    const int mt = mt_beg + min(i, ntiles - 1);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int id = tid + q * kDtStreamThreads, row = id >> 5, kc = (id & 31) * 8;
@@ -283,65 +294,103 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
       *reinterpret_cast<u32x4*>(&As[buf * 64 * kDtLd + row * kDtLd + kc]) = r[q];
     }
   };
-  // tile mt_beg goes straight to LDS; tiles mt + 1 and mt + 2 are in flight in registers while tile mt
-  // multiplies, so a load has two tiles' time to land (indices past the range re-read the last tile)
-  u32x4 rt0[kQ], rt1[kQ];
-  load_tile(mt_beg, rt0);
-  store_tile(0, rt0);
-  load_tile(min(mt_beg + 1, mt_end - 1), rt0);
-  load_tile(min(mt_beg + 2, mt_end - 1), rt1);
-  __syncthreads();
-  int buf = 0;
-  // one tile: multiply LDS[buf], write delta, move the registers' tile into the other buffer and refill
-  // the registers with the tile three ahead
-  auto tile = [&](int mt, u32x4* rg) {
-    f32x4 acc[4][kDtWaveT];
+  typedef f32x4 Acc[4][kDtWaveT];
+  auto mfma_ks = [&](const bf16_t* At, int ks, Acc& acc) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = *reinterpret_cast<const bf16x8*>(&At[(r * 16 + lr) * kDtLd + ks * 32 + lk]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < kDtWaveT; ++t)
+        acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][t], a[r], acc[r][t], 0, 0, 0);
+  };
+  auto zero = [&](Acc& acc) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int t = 0; t < kDtWaveT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bf16_t* At = As + buf * 64 * kDtLd;
+  };
+  auto mfma_tile = [&](int buf, Acc& acc) {
+    zero(acc);
+#pragma unroll
+    for (int ks = 0; ks < kDtMaxR / 32; ++ks) mfma_ks(As + buf * 64 * kDtLd, ks, acc);
+  };
+  // acc[r][t][i2] is channel t*16 + 4*lq + i2 of token r*16 + lr: bias + softplus, four bf16 channels to
+  // the LDS output tile in one 8-byte write
+  auto epilogue_part = [&](bf16_t* O, const Acc& acc, int r, int t) {
+    uint32_t pk[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint32_t lo = f2bf(softplus(acc[r][t][2 * h2] + bs[t][2 * h2]));
+      const uint32_t hi = f2bf(softplus(acc[r][t][2 * h2 + 1] + bs[t][2 * h2 + 1]));
+      pk[h2] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint2*>(&O[(r * 16 + lr) * kDtStreamOutLd + wave * kDtWaveCh + t * 16 + lq * 4]) =
+        make_uint2(pk[0], pk[1]);
+  };
+  // the LDS output tile of tile i as whole rows: 64 rows x 512 bytes, 16 bytes per lane, 4 per thread; the
+  // buffer range ends at the last token and at the last channel of the workgroup's block
+  auto store_out = [&](int i, const bf16_t* O) {
+    const int64_t m0 = (int64_t)(mt_beg + i) * 64;
+    const int rows = min(64, (int)(M - m0));
+    const __amdgpu_buffer_rsrc_t out =
+        __builtin_amdgcn_make_buffer_rsrc(delta + m0 * C, (short)0, rows * C * 2, kDtBufferFlags);
+    const int ch = (tid & 31) * 8, cbase = cb * 256;
+#pragma unroll
+    for (int q = 0; q < 64 * 32 / kDtStreamThreads; ++q) {
+      const int row = (tid >> 5) + q * (kDtStreamThreads / 32);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&O[row * kDtStreamOutLd + ch]);
+      if (cbase + ch < C)
+        __builtin_amdgcn_raw_buffer_store_b128(v, out, (uint32_t)((row * C + cbase + ch) * 2), 0, 0);
+    }
+  };
+  // MFMAs of the tile in LDS buffer buf into acc, interleaved with the epilogue of the previous tile from
+  // prev into output buffer O: K step ks carries epilogue part ks (there are as many parts as K steps)
+  static_assert(4 * kDtWaveT == kDtMaxR / 32, "one epilogue part per K step");
+  auto mfma_and_epilogue = [&](int buf, Acc& acc, bf16_t* O, const Acc& prev) {
+    zero(acc);
 #pragma unroll
     for (int ks = 0; ks < kDtMaxR / 32; ++ks) {
-      bf16x8 a[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = *reinterpret_cast<const bf16x8*>(&At[(r * 16 + lr) * kDtLd + ks * 32 + lk]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < kDtWaveT; ++t)
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][t], a[r], acc[r][t], 0, 0, 0);
+      mfma_ks(As + buf * 64 * kDtLd, ks, acc);
+      epilogue_part(O, prev, ks / kDtWaveT, ks % kDtWaveT);
     }
-    // epilogue: acc[r][t][i2] is channel t*16 + 4*lq + i2 of token r*16 + lr: bias + softplus, four bf16
-    // channels per 8-byte store
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mt * 64 + r * 16 + lr;
-#pragma unroll
-        for (int t = 0; t < kDtWaveT; ++t) {
-          uint32_t pk[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const uint32_t lo = f2bf(softplus(acc[r][t][2 * h2] + bs[t][2 * h2]));
-            const uint32_t hi = f2bf(softplus(acc[r][t][2 * h2 + 1] + bs[t][2 * h2 + 1]));
-            pk[h2] = lo | (hi << 16);
-          }
-          if (m < M)
-            *reinterpret_cast<uint2*>(delta + (int64_t)m * C + c0 + t * 16 + lq * 4) = make_uint2(pk[0], pk[1]);
-        }
-      }
-    }
-    store_tile(buf ^ 1, rg);
-    load_tile(min(mt + 3, mt_end - 1), rg);
-    __syncthreads();
-    buf ^= 1;
   };
-  // unrolled by two so the two register sets alternate without copies
-  for (int mt = mt_beg; mt < mt_end; mt += 2) {
-    tile(mt, rt0);
-    if (mt + 1 >= mt_end) break;
-    tile(mt + 1, rt1);
+
+  // Tile i lives in LDS buffer i & 1 and its output in LDS output buffer i & 1.  Prologue: tile 0 to LDS,
+  // tiles 1 and 2 in flight, MFMAs of tile 0, tile 1 to LDS.  Step i: stores of tile i - 1's output, MFMAs
+  // of tile i + 1 with the epilogue of tile i, tile i + 2 (in registers) into the buffer tile i used, tile
+  // i + 4 requested, barrier.  Unrolled by two, so accumulators and register sets alternate without copies.
+  u32x4 rt0[kQ], rt1[kQ];
+  Acc accA, accB;
+  load_tile(0, rt0);
+  store_tile(0, rt0);
+  load_tile(1, rt0);
+  load_tile(2, rt1);
+  __syncthreads();
+  mfma_tile(0, accA);
+  store_tile(1, rt0);
+  load_tile(3, rt0);
+  __syncthreads();
+  for (int i = 0;; i += 2) {
+    if (i > 0) store_out(i - 1, Os + 64 * kDtStreamOutLd);
+    mfma_and_epilogue(1, accB, Os, accA);            // MFMAs of tile i + 1 (past the group: a re-read), epilogue of i
+    store_tile(0, rt1);                              // tile i + 2
+    load_tile(i + 4, rt1);
+    __syncthreads();
+    if (i + 1 >= ntiles) {
+      store_out(i, Os);
+      break;
+    }
+    store_out(i, Os);
+    mfma_and_epilogue(0, accA, Os + 64 * kDtStreamOutLd, accB);   // MFMAs of tile i + 2, epilogue of tile i + 1
+    store_tile(1, rt0);                              // tile i + 3
+    load_tile(i + 5, rt0);
+    __syncthreads();
+    if (i + 2 >= ntiles) {
+      store_out(i + 1, Os + 64 * kDtStreamOutLd);
+      break;
+    }
   }
 }
 
