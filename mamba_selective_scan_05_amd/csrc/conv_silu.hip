@@ -144,52 +144,65 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T* __restrict__ x,
   }
 }
 
-// One token per sequence (decode): each thread takes 16 bytes of channels, reads their old conv state and
-// the new input, writes xc and the shifted conv state.  The thread reads the state before writing it, so
+// One token per sequence (decode): each thread takes 16 bytes of channels of one sequence; a workgroup takes
+// 256 such groups.  The workgroup's conv state (3 entries per channel, 48 bytes per thread) and conv weights
+// (64 bytes per thread) are read as contiguous 16-byte lanes into LDS and each thread picks its own there
+// (per-lane 48- or 64-byte strides would make every load instruction touch 3-4x as many cache lines); the
+// shifted state goes back through LDS the same way.  The whole block is read before any of it is written, so
 // conv_out may alias conv_in.
 template <typename T>
 __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x, int64_t xs,
                                                         const T* __restrict__ conv_w, const T* __restrict__ conv_b,
                                                         const T* conv_in, T* __restrict__ xc, T* conv_out, int C) {
   constexpr int V = Vec16<T>::n;
-  const int c0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
-  if (c0 >= C) return;
+  __shared__ uint4 sst[256 * (kTaps - 1)], sw[256 * kTaps];
+  const int tid = threadIdx.x;
+  const int cbase = blockIdx.x * 256 * V;
+  const int ng = min(256 * V, C - cbase) / V;          // channel groups of this block (C % 64 == 0)
   const int b = blockIdx.y;
-  float st[(kTaps - 1) * V], cur[V], wf[V * kTaps], bias[V];
-  const int64_t so = ((int64_t)b * C + c0) * (kTaps - 1);
-  if (conv_in) {
-#pragma unroll
-    for (int q = 0; q < kTaps - 1; ++q) load16(conv_in + so + q * V, st + q * V);
-  } else {
-#pragma unroll
-    for (int i = 0; i < (kTaps - 1) * V; ++i) st[i] = 0.0f;
+  const int64_t so = ((int64_t)b * C + cbase) * (kTaps - 1);
+  {
+    const uint4* gst = reinterpret_cast<const uint4*>(conv_in + so);
+    const uint4* gw = reinterpret_cast<const uint4*>(conv_w + (int64_t)cbase * kTaps);
+    for (int k = tid; k < ng * (kTaps - 1); k += 256) sst[k] = conv_in ? gst[k] : make_uint4(0u, 0u, 0u, 0u);
+    for (int k = tid; k < ng * kTaps; k += 256) sw[k] = gw[k];
   }
-  load16(x + (int64_t)b * xs + c0, cur);
+  __syncthreads();
+  if (tid < ng) {
+    const int c0 = cbase + tid * V;
+    float st[(kTaps - 1) * V], cur[V], wf[V * kTaps], bias[V];
 #pragma unroll
-  for (int q = 0; q < V * kTaps; q += V) load16(conv_w + (int64_t)c0 * kTaps + q, wf + q);
-  if (conv_b) {
-    load16(conv_b + c0, bias);
-  } else {
+    for (int q = 0; q < kTaps - 1; ++q) unpack16<T>(sst[tid * (kTaps - 1) + q], st + q * V);
 #pragma unroll
-    for (int i = 0; i < V; ++i) bias[i] = 0.0f;
+    for (int q = 0; q < kTaps; ++q) unpack16<T>(sw[tid * kTaps + q], wf + q * V);
+    load16(x + (int64_t)b * xs + c0, cur);
+    if (conv_b) {
+      load16(conv_b + c0, bias);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) bias[i] = 0.0f;
+    }
+    float o[V], ns[(kTaps - 1) * V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float* s3 = st + i * (kTaps - 1);
+      float u = bias[i];
+      u = fmaf(wf[i * kTaps + 0], s3[0], u);
+      u = fmaf(wf[i * kTaps + 1], s3[1], u);
+      u = fmaf(wf[i * kTaps + 2], s3[2], u);
+      u = fmaf(wf[i * kTaps + 3], cur[i], u);
+      o[i] = silu(u);
+      ns[i * (kTaps - 1) + 0] = s3[1];
+      ns[i * (kTaps - 1) + 1] = s3[2];
+      ns[i * (kTaps - 1) + 2] = cur[i];
+    }
+    store16(xc + (int64_t)b * C + c0, o);
+#pragma unroll
+    for (int q = 0; q < kTaps - 1; ++q) store16(reinterpret_cast<T*>(&sst[tid * (kTaps - 1) + q]), ns + q * V);
   }
-  float o[V], ns[(kTaps - 1) * V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const float* s3 = st + i * (kTaps - 1);
-    float u = bias[i];
-    u = fmaf(wf[i * kTaps + 0], s3[0], u);
-    u = fmaf(wf[i * kTaps + 1], s3[1], u);
-    u = fmaf(wf[i * kTaps + 2], s3[2], u);
-    u = fmaf(wf[i * kTaps + 3], cur[i], u);
-    o[i] = silu(u);
-    ns[i * (kTaps - 1) + 0] = s3[1];
-    ns[i * (kTaps - 1) + 1] = s3[2];
-    ns[i * (kTaps - 1) + 2] = cur[i];
-  }
-  store16(xc + (int64_t)b * C + c0, o);
-#pragma unroll
-  for (int q = 0; q < kTaps - 1; ++q) store16(conv_out + so + q * V, ns + q * V);
+  __syncthreads();
+  uint4* gout = reinterpret_cast<uint4*>(conv_out + so);
+  for (int k = tid; k < ng * (kTaps - 1); k += 256) gout[k] = sst[k];
 }
 
 template <typename T>
