@@ -72,6 +72,40 @@ __device__ __forceinline__ void load_a2(const T* A_log, int c, float* a2) {
   for (int n = 0; n < kN; ++n) a2[n] = -exp2_fast(io<T>::ld(A_log + (int64_t)c * kN + n) * kLog2e) * kLog2e;
 }
 
+// The wave's 64 channels of a [B, C, 16] fp32 state are 4 KB of contiguous memory.  They move between HBM
+// and registers through a 4 KB LDS tile, as four 1 KB rows of contiguous 16-byte lanes: per-lane 64-byte
+// strides would make each 16-byte access instruction touch 32 cache lines for 1 KB of data (this is the
+// whole traffic of a one-token step).  In LDS, chunk q of lane l sits in slot q ^ ((l >> 2) & 3) of the
+// lane's 64 bytes, which keeps the per-lane 16-byte reads and writes free of bank conflicts.
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+__device__ __forceinline__ int hslot(int l, int q) { return l * 16 + ((q ^ ((l >> 2) & 3)) << 2); }
+__device__ __forceinline__ void state_load(const float* src, float* hs, int lane, float* h) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = q * 64 + lane;                      // 16-byte chunk g of the wave's 4 KB
+    *reinterpret_cast<f32x4*>(&hs[hslot(g >> 2, g & 3)]) = *reinterpret_cast<const f32x4*>(src + g * 4);
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&hs[hslot(lane, q)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[q * 4 + i] = v[i];
+  }
+}
+__device__ __forceinline__ void state_store(float* dst, float* hs, int lane, const float* h) {
+  __builtin_amdgcn_wave_barrier();                    // the tile may still be in use by an earlier load
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(&hs[hslot(lane, q)]) = f32x4{h[q * 4], h[q * 4 + 1], h[q * 4 + 2], h[q * 4 + 3]};
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = q * 64 + lane;
+    *reinterpret_cast<f32x4*>(dst + g * 4) = *reinterpret_cast<const f32x4*>(&hs[hslot(g >> 2, g & 3)]);
+  }
+}
+
 // FULL = false: the local pass (end state + delta sum of a piece); FULL = true: the output pass.
 template <typename T, bool FULL>
 __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
@@ -81,6 +115,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   const int L = a.L, C = a.C, P = a.P;
   const int t0 = p * a.Lp, t1 = min(L, t0 + a.Lp);
 
+  __shared__ __attribute__((aligned(16))) float hs[64 * kN];
   float a2[kN], h[kN];
   load_a2((const T*)a.A_log, c, a2);
   if (FULL && P > 1) {
@@ -88,9 +123,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = src[(int64_t)n * C];
   } else if (p == 0 && a.h0) {
-    const float* src = a.h0 + ((int64_t)b * C + c) * kN;
-#pragma unroll
-    for (int n = 0; n < kN; ++n) h[n] = src[n];
+    state_load(a.h0 + ((int64_t)b * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
   } else {
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
@@ -212,9 +245,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     return;
   }
   if (p == P - 1) {
-    float* ho = a.h_out + ((int64_t)b * C + c) * kN;
-#pragma unroll
-    for (int n = 0; n < kN; ++n) ho[n] = h[n];
+    state_store(a.h_out + ((int64_t)b * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
     // conv state (unless the conv step wrote it): the last K-1 entries of the extended input (old state
     // entries when L < K-1).  All three are read before any is written, so conv_out may alias conv_in.
     if (!a.conv_out) return;
