@@ -15,6 +15,12 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+// two values rounded the same way and packed (lo in bits 0-15): one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 template <typename T> struct io;
 template <> struct io<float> {
@@ -41,12 +47,20 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 // SiLU(u) = u / (1 + e^-u).  For u -> -inf the exp overflows to inf and the reciprocal gives 0.
 __device__ __forceinline__ float silu(float u) { return u * rcp_fast(1.0f + exp2_fast(-u * kLog2e)); }
 
+// max(v, 0) as one v_max_f32.  fmaxf on a value the compiler cannot prove canonical (a matrix-core result,
+// a load) first runs it through a second v_max_f32 to quiet signalling NaNs; the inputs here carry none.
+__device__ __forceinline__ float relu(float v) {
+  float r;
+  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 // softplus(v) = log(1 + e^v) = max(v, 0) + log(1 + e^-|v|), without overflow, on the transcendental unit
 // (v_exp_f32, v_log_f32).  For v below about -17, 1 + e^v rounds to 1 and the result is 0 instead of
 // e^v < 4e-8: an absolute error far below anything a delta of that size can change downstream.
 __device__ __forceinline__ float softplus(float v) {
   const float e = exp2_fast(-fabsf(v) * kLog2e);
-  return fmaxf(v, 0.0f) + __builtin_amdgcn_logf(1.0f + e) * kLn2;
+  return relu(v) + __builtin_amdgcn_logf(1.0f + e) * kLn2;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

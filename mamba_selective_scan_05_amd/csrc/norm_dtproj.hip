@@ -250,7 +250,19 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
   const int nmt = (M + 63) / 64;
-  const int g = blockIdx.x % groups, cb = blockIdx.x / groups;
+  // Workgroup i runs on XCD i % 8.  With a multiple of 8 channel blocks, XCD x takes channel blocks x, x + 8,
+  // ... (every token group of each), so its L2 holds only those blocks' W_dt rows: one eighth of W_dt per XCD
+  // instead of all of it (measured: the start-up W_dt load took ~3 us with every XCD fetching the whole).
+  const int ncb = (C + 255) / 256;
+  int g, cb;
+  if (ncb % 8 == 0) {
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+    cb = x + 8 * (j / groups);
+    g = j % groups;
+  } else {
+    g = blockIdx.x % groups;
+    cb = blockIdx.x / groups;
+  }
   const int mt_beg = g * tiles_per_group, mt_end = min(nmt, mt_beg + tiles_per_group);
   if (mt_beg >= mt_end) return;                      // uniform over the workgroup
   const int ntiles = mt_end - mt_beg;
@@ -265,8 +277,9 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
 #pragma unroll
     for (int t = 0; t < kDtWaveT; ++t)
       wa[ks][t] = ld16_guard(w + (int64_t)(cw + t * 16 + lr) * R + ks * 32 + lk, ks * 32 + lk < R);
-  // bias of the four channels this lane's accumulators hold in each channel tile
-  float bs[kDtWaveT][4];
+  // bias of the four channels this lane's accumulators hold in each channel tile: the accumulators start
+  // from it, so the products come out with the bias already added
+  f32x4 bs[kDtWaveT];
 #pragma unroll
   for (int t = 0; t < kDtWaveT; ++t)
 #pragma unroll
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int t = 0; t < kDtWaveT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < kDtWaveT; ++t) acc[r][t] = bs[t];
   };
   auto mfma_tile = [&](int buf, Acc& acc) {
     zero(acc);
@@ -321,11 +334,7 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
   auto epilogue_part = [&](bf16_t* O, const Acc& acc, int r, int t) {
     uint32_t pk[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const uint32_t lo = f2bf(softplus(acc[r][t][2 * h2] + bs[t][2 * h2]));
-      const uint32_t hi = f2bf(softplus(acc[r][t][2 * h2 + 1] + bs[t][2 * h2 + 1]));
-      pk[h2] = lo | (hi << 16);
-    }
+    for (int h2 = 0; h2 < 2; ++h2) pk[h2] = f2bf2(softplus(acc[r][t][2 * h2]), softplus(acc[r][t][2 * h2 + 1]));
     *reinterpret_cast<uint2*>(&O[(r * 16 + lr) * kDtStreamOutLd + wave * kDtWaveCh + t * 16 + lq * 4]) =
         make_uint2(pk[0], pk[1]);
   };
