@@ -25,6 +25,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
     # packed fp32 VALU instructions stay off (the compiler would otherwise form them from float pairs)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: with them in AGPRs the compiler shuffled x_proj's 36
+    # accumulator tiles through copies (~80 v_accvgpr moves per K block; measured 7% slower)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __re
   // one array per stage, so the compiler can tell the loads in flight into one stage from reads of another
   __shared__ __attribute__((aligned(16))) bf16_t As0[kMT * kKB], As1[kMT * kKB], As2[kMT * kKB];
   __shared__ __attribute__((aligned(16))) bf16_t Bs0[kNG * kKB], Bs1[kNG * kKB], Bs2[kNG * kKB];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS destinations in SGPRs
   const int s = blockIdx.x % splits;
   const int m0 = (blockIdx.x / splits) * kMT;
   const int n0 = blockIdx.z * kNG;
@@ -86,29 +87,32 @@ __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __re
   // Load q of this wave fills LDS rows 8 (wave * count + q) .. + 7; lane l takes row + l / 8, slot l % 8, so
   // it reads the global chunk (l % 8) ^ (row & 7).  Rows past M (tokens) or N (columns) re-read the last
   // valid row: they only feed outputs that are never stored.
-  const bf16_t* pa[kAL];
-  const bf16_t* pb[kBL];
+  // Addresses are a wave-uniform tile base plus a 32-bit per-lane byte offset (one SGPR base per load).
+  const char* abase = reinterpret_cast<const char*>(xc + (int64_t)m0 * K);
+  const char* bbase = reinterpret_cast<const char*>(w + (int64_t)n0 * K);
+  uint32_t oa[kAL], ob[kBL];
 #pragma unroll
   for (int q = 0; q < kAL; ++q) {
     const int row = (wave * kAL + q) * 8 + (lane >> 3);
-    pa[q] = xc + (int64_t)min(m0 + row, M - 1) * K + (((lane & 7) ^ (row & 7)) << 3);
+    oa[q] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + (((lane & 7) ^ (row & 7)) << 3)) * 2);
   }
 #pragma unroll
   for (int q = 0; q < kBL; ++q) {
     const int row = (wave * kBL + q) * 8 + (lane >> 3);
-    pb[q] = w + (int64_t)min(n0 + row, N - 1) * K + (((lane & 7) ^ (row & 7)) << 3);
+    ob[q] = (uint32_t)(((int64_t)(min(n0 + row, N - 1) - n0) * K + (((lane & 7) ^ (row & 7)) << 3)) * 2);
   }
-  // block b (past the last one: the last again, into a stage nobody reads) -> stage (A, B)
+  // block b (past the last one: the last again, into a stage nobody reads) -> stage (A, B).  The W_x rows
+  // (L2 hits) are requested before the xc rows (from HBM): measured ~3% faster than the other order.
   auto issue = [&](int b, bf16_t* A, bf16_t* B) {
-    const int kb = kbeg + min(b, nblocks - 1) * kKB;
-#pragma unroll
-    for (int q = 0; q < kAL; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_t*)(pa[q] + kb), (lds_void_t*)(A + (wave * kAL + q) * 8 * kKB),
-                                       16, 0, 0);
+    const int64_t kb = (int64_t)(kbeg + min(b, nblocks - 1) * kKB) * 2;
 #pragma unroll
     for (int q = 0; q < kBL; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_t*)(pb[q] + kb), (lds_void_t*)(B + (wave * kBL + q) * 8 * kKB),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void_t*)(bbase + kb + ob[q]),
+                                       (lds_void_t*)(B + (wave * kBL + q) * 8 * kKB), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kAL; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(abase + kb + oa[q]),
+                                       (lds_void_t*)(A + (wave * kAL + q) * 8 * kKB), 16, 0, 0);
   };
   auto compute = [&](const bf16_t* A, const bf16_t* B) {
 #pragma unroll
