@@ -233,18 +233,20 @@ __global__ __launch_bounds__(256, 2) void dtproj_mfma_kernel(const bf16_t* __res
 // kernel with per-lane 8-byte stores).  Stores go through a per-tile buffer resource whose range ends at the
 // last token, so there are no branches.  Workgroup i runs on XCD i % 8 and takes token-tile group i % G, so
 // each XCD keeps its group's dln tiles in its L2.
-constexpr int kDtStreamWaves = 8;
-constexpr int kDtStreamThreads = 64 * kDtStreamWaves;
-constexpr int kDtWaveCh = 256 / kDtStreamWaves;         // channels per wave
+// NW waves per workgroup, 32 channels per wave: 256 channels per workgroup for long inputs, 128 for a few
+// token tiles (decode), where twice as many workgroups each load half as much of W_dt.
+constexpr int kDtWaveCh = 32;                            // channels per wave
 constexpr int kDtWaveT = kDtWaveCh / 16;                 // 16-channel MFMA tiles per wave
 constexpr int kDtBufferFlags = 0x00020000;               // dword 3 of a raw buffer descriptor on gfx9-family GPUs
-constexpr int kDtStreamOutLd = 256 + 8;                  // padded row of the LDS output tile (bf16)
-__global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel(const bf16_t* __restrict__ dln,
-                                                                               const bf16_t* __restrict__ w,
-                                                                               const bf16_t* __restrict__ bias,
-                                                                               bf16_t* __restrict__ delta, int M,
-                                                                               int C, int R, int groups,
-                                                                               int tiles_per_group) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void dtproj_mfma_stream_kernel(const bf16_t* __restrict__ dln,
+                                                                        const bf16_t* __restrict__ w,
+                                                                        const bf16_t* __restrict__ bias,
+                                                                        bf16_t* __restrict__ delta, int M, int C,
+                                                                        int R, int groups, int tiles_per_group) {
+  constexpr int kDtStreamThreads = 64 * NW;
+  constexpr int kCB = kDtWaveCh * NW;                    // channels per workgroup
+  constexpr int kDtStreamOutLd = kCB + 8;                // padded row of the LDS output tile (bf16)
   __shared__ __attribute__((aligned(16))) bf16_t As[2 * 64 * kDtLd];
   __shared__ __attribute__((aligned(16))) bf16_t Os[2 * 64 * kDtStreamOutLd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
   // Workgroup i runs on XCD i % 8.  With a multiple of 8 channel blocks, XCD x takes channel blocks x, x + 8,
   // ... (every token group of each), so its L2 holds only those blocks' W_dt rows: one eighth of W_dt per XCD
   // instead of all of it (measured: the start-up W_dt load took ~3 us with every XCD fetching the whole).
-  const int ncb = (C + 255) / 256;
+  const int ncb = (C + kCB - 1) / kCB;
   int g, cb;
   if (ncb % 8 == 0) {
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
   const int mt_beg = g * tiles_per_group, mt_end = min(nmt, mt_beg + tiles_per_group);
   if (mt_beg >= mt_end) return;                      // uniform over the workgroup
   const int ntiles = mt_end - mt_beg;
-  const int c0 = cb * 256 + wave * kDtWaveCh;
+  const int c0 = cb * kCB + wave * kDtWaveCh;
   const bool active = c0 < C;
   const int cw = active ? c0 : 0;                    // waves past C read valid rows and store nothing
 
@@ -285,8 +287,8 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) bs[t][i2] = bf2f(bias[cw + t * 16 + lq * 4 + i2]);
 
-  // dln tile loader: 64 rows x 256 k = 2048 chunks of 16 bytes, 4 per thread.  Rows past M re-read row
-  // M - 1 (their products are never stored) and k past R re-reads column R - 8 (finite values that meet
+  // dln tile loader: 64 rows x 256 k = 2048 chunks of 16 bytes, 2048 / threads per thread.  Rows past M
+  // re-read row M - 1 (their products are never stored) and k past R re-reads column R - 8 (finite values that meet
   // the zero W_dt fragments), so the loads need no select, which would stall on them at issue.  Tiles past
   // the group re-read its last tile.
   typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
@@ -338,17 +340,18 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
     *reinterpret_cast<uint2*>(&O[(r * 16 + lr) * kDtStreamOutLd + wave * kDtWaveCh + t * 16 + lq * 4]) =
         make_uint2(pk[0], pk[1]);
   };
-  // the LDS output tile of tile i as whole rows: 64 rows x 512 bytes, 16 bytes per lane, 4 per thread; the
-  // buffer range ends at the last token and at the last channel of the workgroup's block
+  // the LDS output tile of tile i as whole rows: 64 rows x 2 kCB bytes, 16 bytes per lane, 4 per thread;
+  // the buffer range ends at the last token and at the last channel of the workgroup's block
   auto store_out = [&](int i, const bf16_t* O) {
     const int64_t m0 = (int64_t)(mt_beg + i) * 64;
     const int rows = min(64, (int)(M - m0));
     const __amdgpu_buffer_rsrc_t out =
         __builtin_amdgcn_make_buffer_rsrc(delta + m0 * C, (short)0, rows * C * 2, kDtBufferFlags);
-    const int ch = (tid & 31) * 8, cbase = cb * 256;
+    constexpr int kRowChunks = kCB / 8;                  // 16-byte chunks per output row
+    const int ch = (tid % kRowChunks) * 8, cbase = cb * kCB;
 #pragma unroll
-    for (int q = 0; q < 64 * 32 / kDtStreamThreads; ++q) {
-      const int row = (tid >> 5) + q * (kDtStreamThreads / 32);
+    for (int q = 0; q < 64 * kRowChunks / kDtStreamThreads; ++q) {
+      const int row = tid / kRowChunks + q * (kDtStreamThreads / kRowChunks);
       const u32x4 v = *reinterpret_cast<const u32x4*>(&O[row * kDtStreamOutLd + ch]);
       if (cbase + ch < C)
         __builtin_amdgcn_raw_buffer_store_b128(v, out, (uint32_t)((row * C + cbase + ch) * 2), 0, 0);
@@ -364,6 +367,11 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
       mfma_ks(As + buf * 64 * kDtLd, ks, acc);
       epilogue_part(O, prev, ks / kDtWaveT, ks % kDtWaveT);
     }
+  };
+  // the epilogue of the group's last tile, which has no next tile to overlap with
+  auto epilogue_all = [&](bf16_t* O, const Acc& prev) {
+#pragma unroll
+    for (int ks = 0; ks < kDtMaxR / 32; ++ks) epilogue_part(O, prev, ks / kDtWaveT, ks % kDtWaveT);
   };
 
   // Tile i lives in LDS buffer i & 1 and its output in LDS output buffer i & 1.  Prologue: tile 0 to LDS,
@@ -383,23 +391,27 @@ __global__ __launch_bounds__(kDtStreamThreads, 1) void dtproj_mfma_stream_kernel
   __syncthreads();
   for (int i = 0;; i += 2) {
     if (i > 0) store_out(i - 1, Os + 64 * kDtStreamOutLd);
-    mfma_and_epilogue(1, accB, Os, accA);            // MFMAs of tile i + 1 (past the group: a re-read), epilogue of i
-    store_tile(0, rt1);                              // tile i + 2
-    load_tile(i + 4, rt1);
-    __syncthreads();
-    if (i + 1 >= ntiles) {
+    if (i + 1 >= ntiles) {                           // tile i is the group's last
+      epilogue_all(Os, accA);
+      __syncthreads();
       store_out(i, Os);
       break;
     }
+    mfma_and_epilogue(1, accB, Os, accA);            // MFMAs of tile i + 1, epilogue of tile i
+    store_tile(0, rt1);                              // tile i + 2
+    load_tile(i + 4, rt1);
+    __syncthreads();
     store_out(i, Os);
+    if (i + 2 >= ntiles) {                           // tile i + 1 is the group's last
+      epilogue_all(Os + 64 * kDtStreamOutLd, accB);
+      __syncthreads();
+      store_out(i + 1, Os + 64 * kDtStreamOutLd);
+      break;
+    }
     mfma_and_epilogue(0, accA, Os + 64 * kDtStreamOutLd, accB);   // MFMAs of tile i + 2, epilogue of tile i + 1
     store_tile(1, rt0);                              // tile i + 3
     load_tile(i + 5, rt0);
     __syncthreads();
-    if (i + 2 >= ntiles) {
-      store_out(i + 1, Os + 64 * kDtStreamOutLd);
-      break;
-    }
   }
 }
 
@@ -433,14 +445,20 @@ void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, voi
   if (bf16) {
     const int ncb = (C + 255) / 256, nmt = (M + 63) / 64;
     if (R <= kDtMaxR) {
-      // one workgroup per CU: enough token-tile groups for ~256 workgroups, 8 when possible (one per XCD)
-      int groups = ncb >= 256 ? 1 : 256 / ncb;
+      // one workgroup per CU: enough token-tile groups for ~256 workgroups, 8 when possible (one per XCD).
+      // With at most 8 token tiles the workgroups take 128 channels instead of 256.
+      const bool narrow = nmt <= 8;
+      const int nb = narrow ? (C + 127) / 128 : ncb;
+      int groups = nb >= 256 ? 1 : 256 / nb;
       if (groups > 8) groups = groups / 8 * 8;
       if (groups > nmt) groups = nmt;
       const int per = (nmt + groups - 1) / groups;
-      hipLaunchKernelGGL(dtproj_mfma_stream_kernel, dim3(ncb * groups), dim3(kDtStreamThreads), 0, st,
-                         (const bf16_t*)dln,
-                         (const bf16_t*)w, (const bf16_t*)b, (bf16_t*)delta, M, C, R, groups, per);
+      if (narrow)
+        hipLaunchKernelGGL(dtproj_mfma_stream_kernel<4>, dim3(nb * groups), dim3(256), 0, st, (const bf16_t*)dln,
+                           (const bf16_t*)w, (const bf16_t*)b, (bf16_t*)delta, M, C, R, groups, per);
+      else
+        hipLaunchKernelGGL(dtproj_mfma_stream_kernel<8>, dim3(nb * groups), dim3(512), 0, st, (const bf16_t*)dln,
+                           (const bf16_t*)w, (const bf16_t*)b, (bf16_t*)delta, M, C, R, groups, per);
     } else {
       hipLaunchKernelGGL(dtproj_mfma_kernel, dim3(ncb * nmt), dim3(256), 0, st, (const bf16_t*)dln, (const bf16_t*)w,
                          (const bf16_t*)b, (bf16_t*)delta, M, C, R);

@@ -94,6 +94,14 @@ def test_bf16_wide_xproj_tiles_across_sequences(with_state):
     _run_and_check(cfg, with_state=with_state, row_stride=528)
 
 
+@pytest.mark.parametrize("B,L", [(1, 450), (2, 155)])
+def test_bf16_few_token_tiles_dt_proj(B, L):
+    # at most 8 64-token tiles: dt_proj takes 128-channel workgroups; at d_inner 8192 they hold two tiles
+    # each (the first case) or one or two with an empty last group (the second), with a ragged last tile
+    cfg = _small(f"few_tiles_B{B}_L{L}", B, L, 8192, 256, "bf16", 22)
+    _run_and_check(cfg)
+
+
 @pytest.mark.parametrize("L", [0, 1, 2, 3, 5, 64, 65])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_short_sequences_and_conv_state(L, io):
