@@ -144,65 +144,93 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T* __restrict__ x,
   }
 }
 
-// One token per sequence (decode): each thread takes 16 bytes of channels of one sequence; a workgroup takes
-// 256 such groups.  The workgroup's conv state (3 entries per channel, 48 bytes per thread) and conv weights
-// (64 bytes per thread) are read as contiguous 16-byte lanes into LDS and each thread picks its own there
-// (per-lane 48- or 64-byte strides would make every load instruction touch 3-4x as many cache lines); the
-// shifted state goes back through LDS the same way.  The whole block is read before any of it is written, so
-// conv_out may alias conv_in.
-template <typename T>
+// One token per sequence (decode): each thread takes 16 bytes of channels; a workgroup takes 256 such groups
+// of SPB consecutive sequences.  The conv weights (64 bytes per thread) are read once per workgroup, as
+// contiguous 16-byte lanes into LDS, and kept in registers for all its sequences.  A sequence's conv state
+// (48 bytes per thread) likewise arrives as contiguous 16-byte lanes, goes through LDS to the thread that
+// owns it, and the shifted state goes back the same way: per-lane 48- or 64-byte strides would make every
+// load instruction touch 3-4x as many cache lines.  The next sequence's state and input are in flight while
+// the current one computes (with SPB > 1).  Each sequence's whole block is read before any of it is
+// written, so conv_out may alias conv_in.
+template <typename T, int SPB>
 __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x, int64_t xs,
                                                         const T* __restrict__ conv_w, const T* __restrict__ conv_b,
-                                                        const T* conv_in, T* __restrict__ xc, T* conv_out, int C) {
+                                                        const T* conv_in, T* __restrict__ xc, T* conv_out, int B,
+                                                        int C) {
   constexpr int V = Vec16<T>::n;
-  __shared__ uint4 sst[256 * (kTaps - 1)], sw[256 * kTaps];
+  constexpr int S3 = kTaps - 1;
+  __shared__ uint4 sst[256 * S3], sw[256 * kTaps];
   const int tid = threadIdx.x;
   const int cbase = blockIdx.x * 256 * V;
   const int ng = min(256 * V, C - cbase) / V;          // channel groups of this block (C % 64 == 0)
-  const int b = blockIdx.y;
-  const int64_t so = ((int64_t)b * C + cbase) * (kTaps - 1);
+  const int b0 = blockIdx.y * SPB;
+  const int nb = min(SPB, B - b0);
+  const int own = min(tid, ng - 1);                     // threads past the block recompute its last group
   {
-    const uint4* gst = reinterpret_cast<const uint4*>(conv_in + so);
     const uint4* gw = reinterpret_cast<const uint4*>(conv_w + (int64_t)cbase * kTaps);
-    for (int k = tid; k < ng * (kTaps - 1); k += 256) sst[k] = conv_in ? gst[k] : make_uint4(0u, 0u, 0u, 0u);
     for (int k = tid; k < ng * kTaps; k += 256) sw[k] = gw[k];
   }
+  float bias[V];
+  if (conv_b) {
+    load16(conv_b + cbase + own * V, bias);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) bias[i] = 0.0f;
+  }
   __syncthreads();
-  if (tid < ng) {
-    const int c0 = cbase + tid * V;
-    float st[(kTaps - 1) * V], cur[V], wf[V * kTaps], bias[V];
+  float wf[V * kTaps];
 #pragma unroll
-    for (int q = 0; q < kTaps - 1; ++q) unpack16<T>(sst[tid * (kTaps - 1) + q], st + q * V);
+  for (int q = 0; q < kTaps; ++q) unpack16<T>(sw[own * kTaps + q], wf + q * V);
+
+  // sequence s: state chunks tid, tid + 256, tid + 512 (clamped to the block; zeros without a state) and the
+  // thread's 16 bytes of input
+  uint4 rs[S3], rx;
+  auto load_seq = [&](int s) {
+    const int64_t b = b0 + s;
+    const uint4* gst = reinterpret_cast<const uint4*>(conv_in + (b * C + cbase) * S3);
 #pragma unroll
-    for (int q = 0; q < kTaps; ++q) unpack16<T>(sw[tid * kTaps + q], wf + q * V);
-    load16(x + (int64_t)b * xs + c0, cur);
-    if (conv_b) {
-      load16(conv_b + c0, bias);
-    } else {
+    for (int q = 0; q < S3; ++q) rs[q] = conv_in ? gst[min(tid + 256 * q, ng * S3 - 1)] : make_uint4(0u, 0u, 0u, 0u);
+    rx = *reinterpret_cast<const uint4*>(x + b * xs + cbase + own * V);
+  };
+  load_seq(0);
+  for (int s = 0; s < nb; ++s) {
+    const int64_t b = b0 + s;
 #pragma unroll
-      for (int i = 0; i < V; ++i) bias[i] = 0.0f;
-    }
-    float o[V], ns[(kTaps - 1) * V];
+    for (int q = 0; q < S3; ++q)
+      if (tid + 256 * q < ng * S3) sst[tid + 256 * q] = rs[q];
+    const uint4 xcur = rx;
+    __syncthreads();
+    if (SPB > 1) load_seq(min(s + 1, nb - 1));         // the last sequence re-reads itself
+    float st[S3 * V], cur[V];
+#pragma unroll
+    for (int q = 0; q < S3; ++q) unpack16<T>(sst[own * S3 + q], st + q * V);
+    unpack16<T>(xcur, cur);
+    float o[V], ns[S3 * V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const float* s3 = st + i * (kTaps - 1);
+      const float* s3 = st + i * S3;
       float u = bias[i];
       u = fmaf(wf[i * kTaps + 0], s3[0], u);
       u = fmaf(wf[i * kTaps + 1], s3[1], u);
       u = fmaf(wf[i * kTaps + 2], s3[2], u);
       u = fmaf(wf[i * kTaps + 3], cur[i], u);
       o[i] = silu(u);
-      ns[i * (kTaps - 1) + 0] = s3[1];
-      ns[i * (kTaps - 1) + 1] = s3[2];
-      ns[i * (kTaps - 1) + 2] = cur[i];
+      ns[i * S3 + 0] = s3[1];
+      ns[i * S3 + 1] = s3[2];
+      ns[i * S3 + 2] = cur[i];
     }
-    store16(xc + (int64_t)b * C + c0, o);
+    __syncthreads();                                    // every thread has read its state from sst
+    if (tid < ng) {
+      store16(xc + b * C + cbase + tid * V, o);
 #pragma unroll
-    for (int q = 0; q < kTaps - 1; ++q) store16(reinterpret_cast<T*>(&sst[tid * (kTaps - 1) + q]), ns + q * V);
+      for (int q = 0; q < S3; ++q) store16(reinterpret_cast<T*>(&sst[tid * S3 + q]), ns + q * V);
+    }
+    __syncthreads();
+    uint4* gout = reinterpret_cast<uint4*>(conv_out + (b * C + cbase) * S3);
+#pragma unroll
+    for (int q = 0; q < S3; ++q)
+      if (tid + 256 * q < ng * S3) gout[tid + 256 * q] = sst[tid + 256 * q];
   }
-  __syncthreads();
-  uint4* gout = reinterpret_cast<uint4*>(conv_out + so);
-  for (int k = tid; k < ng * (kTaps - 1); k += 256) gout[k] = sst[k];
 }
 
 template <typename T>
@@ -239,15 +267,17 @@ void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, 
 
 void launch_conv_step(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
                       const void* conv_in, void* xc, void* conv_out, int B, int C, hipStream_t st) {
+  constexpr int kSeqPerBlock = 1;   // measured at B = 256: 7.1 us, against 7.8 (2) and 9.5 (4): parallelism wins
   const int V = bf16 ? 8 : 4;
-  dim3 grid((C / V + 255) / 256, B);
+  dim3 grid((C / V + 255) / 256, (B + kSeqPerBlock - 1) / kSeqPerBlock);
   if (bf16)
-    hipLaunchKernelGGL(conv_step_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, xs,
+    hipLaunchKernelGGL((conv_step_kernel<bf16_t, kSeqPerBlock>), grid, dim3(256), 0, st, (const bf16_t*)x, xs,
                        (const bf16_t*)conv_w, (const bf16_t*)conv_b, (const bf16_t*)conv_in, (bf16_t*)xc,
-                       (bf16_t*)conv_out, C);
+                       (bf16_t*)conv_out, B, C);
   else
-    hipLaunchKernelGGL(conv_step_kernel<float>, grid, dim3(256), 0, st, (const float*)x, xs, (const float*)conv_w,
-                       (const float*)conv_b, (const float*)conv_in, (float*)xc, (float*)conv_out, C);
+    hipLaunchKernelGGL((conv_step_kernel<float, kSeqPerBlock>), grid, dim3(256), 0, st, (const float*)x, xs,
+                       (const float*)conv_w, (const float*)conv_b, (const float*)conv_in, (float*)xc,
+                       (float*)conv_out, B, C);
 }
 
 void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,

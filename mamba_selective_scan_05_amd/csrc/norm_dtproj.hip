@@ -20,37 +20,65 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-// norm: one wave per token.  S (the number of x_proj slices) and COLS (columns per lane, 64 columns apart)
-// are compile-time so that every partial-sum load is unconditional (columns past W re-read column W - 1
-// and are dropped): all of a lane's loads are in flight together, then added in slice order.
-template <typename T, int S, int COLS>
+// norm: WPT waves per token (1, or 4 when there are few tokens), each summing S / WPT of the x_proj slices.
+// S (the number of slices) and COLS (columns per lane, 64 columns apart) are compile-time so that every
+// partial-sum load is unconditional (columns past W re-read column W - 1 and are dropped): all of a lane's
+// loads are in flight together, then added in slice order; with WPT = 4 the four waves' sums are added in
+// wave order through LDS (a fixed order: the result does not depend on timing).
+template <typename T, int S, int COLS, int WPT>
 __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ part, int M, int R, int N,
                                                    const T* __restrict__ wdt, const T* __restrict__ wb,
                                                    const T* __restrict__ wc, float eps, T* __restrict__ dln,
                                                    float* __restrict__ bc) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (m >= M) return;
+  static_assert(WPT == 1 || WPT == 4, "one wave per token or a whole workgroup per token");
+  constexpr int SW = S / WPT;                          // slices per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = WPT == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
+  if (WPT == 1 && m >= M) return;
+  const int sub = WPT == 1 ? 0 : wave;
   const int W = R + 2 * N;
   const int64_t slice = (int64_t)M * W;
-  const float* src = part + (int64_t)m * W;
-  float pv[COLS][S];
+  const float* src = part + (int64_t)m * W + (int64_t)sub * SW * slice;
+  float pv[COLS][SW], wn[COLS];
 #pragma unroll
   for (int i = 0; i < COLS; ++i) {
     const int col = min(lane + 64 * i, W - 1);
 #pragma unroll
-    for (int p = 0; p < S; ++p) pv[i][p] = src[p * slice + col];
+    for (int p = 0; p < SW; ++p) pv[i][p] = src[p * slice + col];
+  }
+  // the norm weight of each column, loaded with the partial sums (clamped indices, no branches) so that it
+  // is not a second round trip to memory after the reduction
+#pragma unroll
+  for (int i = 0; i < COLS; ++i) {
+    const int col = lane + 64 * i;
+    const float a = io<T>::ld(wdt + min(col, R - 1));
+    const float b = io<T>::ld(wb + min(max(col - R, 0), N - 1));
+    const float c = io<T>::ld(wc + min(max(col - R - N, 0), N - 1));
+    wn[i] = col < R ? a : col < R + N ? b : c;
   }
   float v[COLS];
+#pragma unroll
+  for (int i = 0; i < COLS; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < SW; ++p) s += pv[i][p];
+    v[i] = s;
+  }
+  if (WPT > 1) {
+    __shared__ float red[4][COLS * 64];
+#pragma unroll
+    for (int i = 0; i < COLS; ++i) red[wave][i * 64 + lane] = v[i];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int i = 0; i < COLS; ++i)
+      v[i] = ((red[0][i * 64 + lane] + red[1][i * 64 + lane]) + red[2][i * 64 + lane]) + red[3][i * 64 + lane];
+  }
   float ss_dt = 0.f, ss_b = 0.f, ss_c = 0.f;
 #pragma unroll
   for (int i = 0; i < COLS; ++i) {
     const int col = lane + 64 * i;
-    float s = 0.f;
-#pragma unroll
-    for (int p = 0; p < S; ++p) s += pv[i][p];
-    v[i] = s;
-    const float sq = s * s;
+    const float sq = v[i] * v[i];
     if (col < R) ss_dt += sq;
     else if (col < R + N) ss_b += sq;
     else if (col < W) ss_c += sq;
@@ -65,23 +93,23 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
   for (int i = 0; i < COLS; ++i) {
     const int col = lane + 64 * i;
     if (col < R) {
-      io<T>::st(dln + (int64_t)m * R + col, v[i] * r_dt * io<T>::ld(wdt + col));
+      io<T>::st(dln + (int64_t)m * R + col, v[i] * r_dt * wn[i]);
     } else if (col < R + N) {
-      bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_b * io<T>::ld(wb + (col - R));
+      bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_b * wn[i];
     } else if (col < W) {
-      bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_c * io<T>::ld(wc + (col - R - N));
+      bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_c * wn[i];
     }
   }
 }
 
-template <typename T, int COLS>
+template <typename T, int COLS, int WPT>
 void launch_norm_cols(int splits, dim3 grid, hipStream_t st, const float* part, int M, int R, int N, const T* wdt,
                       const T* wb, const T* wc, float eps, T* dln, float* bc) {
   switch (splits) {
 #define JM_NORM_CASE(S)                                                                                       \
   case S:                                                                                                     \
-    hipLaunchKernelGGL((norm_kernel<T, S, COLS>), grid, dim3(256), 0, st, part, M, R, N, wdt, wb, wc, eps, dln, \
-                       bc);                                                                                   \
+    hipLaunchKernelGGL((norm_kernel<T, S, COLS, (S >= WPT ? WPT : 1)>), grid, dim3(256), 0, st, part, M, R, N, \
+                       wdt, wb, wc, eps, dln, bc);                                                            \
     break;
     JM_NORM_CASE(1)
     JM_NORM_CASE(2)
@@ -93,14 +121,23 @@ void launch_norm_cols(int splits, dim3 grid, hipStream_t st, const float* part, 
   }
 }
 
+template <typename T, int COLS>
+void launch_norm_w(int splits, int M, int R, int N, const T* wdt, const T* wb, const T* wc, float eps, T* dln,
+                   float* bc, const float* part, hipStream_t st) {
+  // few tokens with many slices (decode): a workgroup per token, so that enough waves are in flight
+  if (M <= 1024 && splits >= 4)
+    launch_norm_cols<T, COLS, 4>(splits, dim3(M), st, part, M, R, N, wdt, wb, wc, eps, dln, bc);
+  else
+    launch_norm_cols<T, COLS, 1>(splits, dim3((M + 3) / 4), st, part, M, R, N, wdt, wb, wc, eps, dln, bc);
+}
+
 template <typename T>
 void launch_norm_t(int splits, int M, int R, int N, const T* wdt, const T* wb, const T* wc, float eps, T* dln,
                    float* bc, const float* part, hipStream_t st) {
-  dim3 grid((M + 3) / 4);
   if (R + 2 * N <= 5 * 64)
-    launch_norm_cols<T, 5>(splits, grid, st, part, M, R, N, wdt, wb, wc, eps, dln, bc);
+    launch_norm_w<T, 5>(splits, M, R, N, wdt, wb, wc, eps, dln, bc, part, st);
   else
-    launch_norm_cols<T, 9>(splits, grid, st, part, M, R, N, wdt, wb, wc, eps, dln, bc);
+    launch_norm_w<T, 9>(splits, M, R, N, wdt, wb, wc, eps, dln, bc, part, st);
 }
 
 constexpr int kDtMaxR = 256;            // dt_rank of the staged bf16 path (larger ranks loop in slices)
