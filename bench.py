@@ -123,6 +123,13 @@ def measured_traffic(workload: str, kernel: str):
     return int(meta["bytes_per_launch"])
 
 
+def percentiles(vals_ms):
+    """p10 / p50 / p90 of per-step times, in microseconds (nearest rank)."""
+    v = sorted(vals_ms)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"p10": round(pick(0.1) * 1e3, 2), "p50": round(pick(0.5) * 1e3, 2), "p90": round(pick(0.9) * 1e3, 2)}
+
+
 def stage_groups(stage_ms):
     return {
         "conv_silu": stage_ms["conv_silu"],
@@ -186,13 +193,16 @@ def time_prefill(jm, cfg, steps, warmup, hip):
             raise jm.JMError(s, "jm_mixer_prefill_profiled")
     torch.cuda.synchronize()
     stage_ms = {n: 0.0 for n in names}
+    per_step = []
     for k in range(steps):
         base = k * (nst + 1)
         for i, n in enumerate(names):
             stage_ms[n] += hip.elapsed_ms(evs[base + i], evs[base + i + 1]) / steps
+        per_step.append(hip.elapsed_ms(evs[base], evs[base + nst]))
     hip.destroy(evs)
     lay = jm.workspace_layout(dims)
-    return {"ms": ms, "wall_s": wall, "stage_ms": stage_ms, "splits": lay.dbc_splits, "pieces": lay.scan_chunks}
+    return {"ms": ms, "wall_s": wall, "stage_ms": stage_ms, "splits": lay.dbc_splits, "pieces": lay.scan_chunks,
+            "step_pct": percentiles(per_step)}
 
 
 def time_decode(jm, cfg, steps, warmup, hip):
@@ -251,12 +261,14 @@ def time_decode(jm, cfg, steps, warmup, hip):
             raise jm.JMError(s, "jm_mixer_decode_step_profiled")
     torch.cuda.synchronize()
     stage_ms = {n: 0.0 for n in names}
+    per_step = []
     for k in range(steps):
         base = k * (nst + 1)
         for i, n in enumerate(names):
             stage_ms[n] += hip.elapsed_ms(evs[base + i], evs[base + i + 1]) / steps
+        per_step.append(hip.elapsed_ms(evs[base], evs[base + nst]))
     hip.destroy(evs)
-    return {"ms": ms, "stage_ms": stage_ms}
+    return {"ms": ms, "stage_ms": stage_ms, "step_pct": percentiles(per_step)}
 
 
 def cpu_baseline(cfg, max_tokens):
@@ -292,6 +304,7 @@ def run_decode(jm, dcfg, args, hip):
             "batch": dcfg.batch, "us_per_step": round(dec["ms"] * 1e3, 2),
             "tokens_per_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "alg_bytes": db,
             "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "step_us_events": dec["step_pct"],
             "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()}}
 
 
@@ -387,6 +400,8 @@ def main():
                    "state": "fp32", "x_proj_splits": pre["splits"], "scan_pieces": pre["pieces"]},
         "roofline": roofline,
         "stages": stages,
+        # per-step times of the second (event-instrumented) pass: the events between kernels add a little
+        "step_us_events": pre["step_pct"],
         "mixer_GB_s": round(sum(alg.values()) / (pre["ms"] * 1e-3) / 1e9, 1),
     }
     if not args.no_decode:
