@@ -17,6 +17,13 @@ Distributions (the second argument of N is a variance):
     dt/B/C norm w   = 1, eps = 1e-6
     decode h0       ~ N(0, 0.1) fp32, conv0 ~ N(0, 1) in the I/O dtype
 
+The whole Mamba layer around the mixer (pre-norm, in_proj, mixer, out_proj, residual) adds, with d_model
+the residual width (4096 in Jamba v0.1):
+    x_res           ~ N(0, 1)                 [B, L, d_model]
+    layer norm w    ~ 1 + U(-0.5, 0.5)        [d_model], eps = 1e-6
+    in_proj_w       ~ N(0, 1/d_model)         [2 d_inner, d_model], rows ordered x | z
+    out_proj_w      ~ N(0, 1/d_inner)         [d_model, d_inner]
+
 Every tensor draws from its own torch generator whose seed is a child of numpy's SeedSequence(1000 + cfg),
 spawned in a fixed order, so a tensor's values do not depend on which other tensors were generated.
 """
@@ -34,6 +41,7 @@ import torch
 _TENSOR_ORDER = (
     "x", "z", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D",
     "dt_norm_w", "b_norm_w", "c_norm_w", "conv_state", "ssm_state", "x_steps", "z_steps",
+    "layer_norm_w", "in_proj_w", "out_proj_w", "x_res", "x_res_steps",
 )
 
 
@@ -53,6 +61,7 @@ class MixerConfig:
     decode_steps: int = 0           # > 0: a decode workload of this many single-token steps
     with_state: bool = False        # draw an initial conv / SSM state (decode workloads always do)
     seed: int = 1000
+    d_model: int = 0                # residual width of the whole layer (0: the mixer alone)
 
     @property
     def width(self) -> int:
@@ -161,6 +170,36 @@ def make_decode_tokens(cfg: MixerConfig, device: str = "cpu") -> Dict[str, torch
     x = _normal((B, T, C), 1.0, s["x_steps"], device).to(cfg.torch_dtype)
     z = _normal((B, T, C), 1.0, s["z_steps"], device).to(cfg.torch_dtype)
     return {"x": x, "z": z}
+
+
+# The whole Mamba layer at Jamba v0.1's widths (d_model 4096 around d_inner 8192): 4K prefill and decode.
+LAYER_CONFIGS = (
+    CONFIGS[1].replace(name="jamba_layer_prefill_B1_L4096", d_model=4096, seed=1101),
+    CONFIGS[4].replace(name="jamba_layer_decode_B256", d_model=4096, seed=1104),
+)
+
+
+def make_layer_weights(cfg: MixerConfig, device: str = "cpu") -> Dict[str, torch.Tensor]:
+    """The layer's own weights (pre-norm, in_proj, out_proj) in the I/O dtype; the mixer's come from
+    make_weights.  Drawn on the CPU generator, like the mixer's."""
+    assert cfg.d_model > 0
+    s = _child_seeds(cfg.seed)
+    C, Dm = cfg.d_inner, cfg.d_model
+    w = {
+        "norm_w": _uniform((Dm,), 0.5, 1.5, s["layer_norm_w"], "cpu"),
+        "in_proj_w": _normal((2 * C, Dm), math.sqrt(1.0 / Dm), s["in_proj_w"], "cpu"),
+        "out_proj_w": _normal((Dm, C), math.sqrt(1.0 / C), s["out_proj_w"], "cpu"),
+    }
+    return {k: v.to(cfg.torch_dtype).contiguous().to(device) for k, v in w.items()}
+
+
+def make_layer_input(cfg: MixerConfig, device: str = "cpu", steps: int = 0) -> torch.Tensor:
+    """The residual stream entering the layer: [B, L, d_model], or [B, steps, d_model] decode tokens."""
+    assert cfg.d_model > 0
+    s = _child_seeds(cfg.seed)
+    if steps:
+        return _normal((cfg.batch, steps, cfg.d_model), 1.0, s["x_res_steps"], device).to(cfg.torch_dtype)
+    return _normal((cfg.batch, cfg.seqlen, cfg.d_model), 1.0, s["x_res"], device).to(cfg.torch_dtype)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

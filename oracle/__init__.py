@@ -1,8 +1,12 @@
-"""fp64 CPU oracle of the Jamba Mamba-1 mixer.
+"""fp64 CPU oracle of the Jamba Mamba-1 mixer and of the whole Mamba layer around it.
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU-baseline leg use it.  It shares
 no code with the HIP library and never imports it.
 """
 
+from .layer import *  # noqa: F401,F403
+from .layer import __all__ as _layer_all
 from .mixer import *  # noqa: F401,F403
-from .mixer import __all__  # noqa: F401
+from .mixer import __all__ as _mixer_all
+
+__all__ = list(_mixer_all) + list(_layer_all)
