@@ -1,4 +1,4 @@
-"""ctypes binding of libjm_mixer.so (the C ABI in include/jm_mixer.h).
+"""ctypes binding of libjm_mixer.so (the C ABI in include/jm_mixer.h and include/jm_layer.h).
 
 The functions here only marshal arguments: torch tensors provide device memory and the stream, their
 data pointers go to the library, and every step of the mixer runs in the library's HIP kernels.  If the
@@ -49,6 +49,17 @@ class WorkspaceLayout(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class LayerDims(ctypes.Structure):
+    _fields_ = [("mixer", Dims), ("d_model", ctypes.c_int32), ("layer_norm_eps", ctypes.c_float)]
+
+
+LAYER_WEIGHT_NAMES = ("norm_w", "in_proj_w", "out_proj_w")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES] + [("mixer", Weights)]
+
+
 _lib = None
 
 
@@ -78,6 +89,14 @@ def lib() -> ctypes.CDLL:
             f.restype = I
         L.jm_stage_name.argtypes = [I]
         L.jm_stage_name.restype = ctypes.c_char_p
+        for name in ("jm_layer_prefill", "jm_layer_decode_step"):
+            f = getattr(L, name)
+            f.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, V, V, V, S, V]
+            f.restype = I
+        for name in ("jm_layer_prefill_workspace_size", "jm_layer_decode_workspace_size"):
+            f = getattr(L, name)
+            f.argtypes = [P(LayerDims)]
+            f.restype = S
         _lib = L
     return _lib
 
@@ -235,3 +254,84 @@ class Mixer:
         if s != JM_OK:
             raise JMError(s, "jm_mixer_decode_step")
         return out, conv_state_out, ssm_state_out
+
+
+def make_layer_dims(batch: int, seqlen: int, d_inner: int, dt_rank: int, io_dtype: int, d_model: int,
+                    d_state: int = 16, d_conv: int = 4, norm_eps: float = 1e-6,
+                    layer_norm_eps: float = 1e-6) -> LayerDims:
+    return LayerDims(make_dims(batch, seqlen, d_inner, dt_rank, io_dtype, d_state, d_conv, norm_eps), d_model,
+                     layer_norm_eps)
+
+
+def layer_workspace_size(dims: LayerDims, decode: bool = False) -> int:
+    f = lib().jm_layer_decode_workspace_size if decode else lib().jm_layer_prefill_workspace_size
+    return int(f(ctypes.byref(dims)))
+
+
+def call_layer(dims: LayerDims, weights: LayerWeights, x_res, out, conv_in, conv_out, h_in, h_out, ws,
+               ws_bytes: int, stream: int, decode: bool = False) -> int:
+    """The raw layer entry point on integer device pointers (None for NULL)."""
+    f = lib().jm_layer_decode_step if decode else lib().jm_layer_prefill
+    return f(_ref(dims), _ref(weights), x_res, out, conv_in, conv_out, h_in, h_out, ws, ws_bytes, stream)
+
+
+class Layer:
+    """The whole Mamba layer (pre-norm, in_proj, mixer, out_proj, residual): holds the layer's and the mixer's
+    weights (device tensors in the I/O dtype) and a reusable workspace."""
+
+    def __init__(self, layer_weights: Dict[str, torch.Tensor], mixer_weights: Dict[str, torch.Tensor], dt_rank: int,
+                 d_state: int = 16, d_conv: int = 4, norm_eps: float = 1e-6, layer_norm_eps: float = 1e-6):
+        self.mixer = Mixer(mixer_weights, dt_rank, d_state, d_conv, norm_eps)
+        self.lw = {k: v.contiguous() for k, v in layer_weights.items()}
+        self.packed = LayerWeights(*[_ptr(self.lw[n]) for n in LAYER_WEIGHT_NAMES], self.mixer.packed)
+        self.d_model = self.lw["norm_w"].shape[0]
+        self.layer_eps = layer_norm_eps
+        self.device, self.dtype = self.mixer.device, self.mixer.dtype
+        self._ws = None
+
+    def dims(self, batch: int, seqlen: int) -> LayerDims:
+        m = self.mixer
+        return make_layer_dims(batch, seqlen, m.d_inner, m.dt_rank, _io_dtype(m.w["conv_w"]), self.d_model,
+                               m.d_state, m.d_conv, m.eps, self.layer_eps)
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def _run(self, x_res, conv_state, ssm_state, out, conv_state_out, ssm_state_out, decode: bool):
+        B = x_res.shape[0]
+        L = 1 if decode else x_res.shape[1]
+        C = self.mixer.d_inner
+        dims = self.dims(B, L)
+        nbytes = layer_workspace_size(dims, decode)
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_layer_*_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.empty_like(x_res)
+        if conv_state_out is None:
+            conv_state_out = torch.empty((B, C, self.mixer.d_conv - 1), dtype=self.dtype, device=self.device)
+        if ssm_state_out is None:
+            ssm_state_out = torch.empty((B, C, self.mixer.d_state), dtype=torch.float32, device=self.device)
+        _check_contiguous(x_res=x_res, out=out, conv_state=conv_state, conv_state_out=conv_state_out,
+                          ssm_state=ssm_state, ssm_state_out=ssm_state_out)
+        s = call_layer(dims, self.packed, _ptr(x_res), _ptr(out), _ptr(conv_state), _ptr(conv_state_out),
+                       _ptr(ssm_state), _ptr(ssm_state_out), _ptr(ws), ws.numel(), _stream(self.device), decode)
+        if s != JM_OK:
+            raise JMError(s, "jm_layer_decode_step" if decode else "jm_layer_prefill")
+        return out, conv_state_out, ssm_state_out
+
+    def prefill(self, x_res: torch.Tensor, conv_state: Optional[torch.Tensor] = None,
+                ssm_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                conv_state_out: Optional[torch.Tensor] = None, ssm_state_out: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """x_res [B, L, d_model] -> (out, conv_state_out, ssm_state_out); out may be x_res itself."""
+        return self._run(x_res, conv_state, ssm_state, out, conv_state_out, ssm_state_out, False)
+
+    def decode_step(self, x_res: torch.Tensor, conv_state: torch.Tensor, ssm_state: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, in_place: bool = False
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """x_res [B, d_model]; with in_place=True the states are updated in place."""
+        co, so = (conv_state, ssm_state) if in_place else (None, None)
+        return self._run(x_res, conv_state, ssm_state, out, co, so, True)

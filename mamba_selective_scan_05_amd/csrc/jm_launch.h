@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "jm_mixer.h"
+
 namespace jm {
 
 // Causal depthwise conv1d (K = 4) + bias + SiLU over [B, L, C] -> xc [B*L, C] (contiguous).
@@ -57,6 +59,17 @@ struct ScanArgs {
 // The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.
 // marks (optional): events recorded before the local pass, the carry pass and the full pass.
 void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks = nullptr);
+
+// The mixer behind jm_mixer_prefill / jm_mixer_decode_step, for the layer entry points: the workspace bytes
+// of a call (a negative jm_status for invalid dims), every check of a call without launching anything, and
+// the validated call itself (each a jm_status).
+int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode);
+int mixer_validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+                   const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+                   bool decode);
+int mixer_run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+              const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+              void* stream, bool decode);
 
 // seqlen == 0: copy the states through (zeros for a NULL input).
 void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,

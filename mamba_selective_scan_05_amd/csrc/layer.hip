@@ -1,0 +1,257 @@
+// The whole Jamba Mamba layer around the mixer (jm_layer.h): pre-norm RMSNorm, in_proj, the mixer,
+// out_proj and the residual add.  The two projections are plain GEMMs and go to hipBLASLt; the norm is a
+// kernel here; the mixer is this library's own.
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "jm_device.h"
+#include "jm_launch.h"
+#include "jm_layer.h"
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kGemmWorkspace = 32ll << 20;   // hipBLASLt workspace carved from the caller's
+constexpr int kMaxDevices = 64;
+
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------------------------------------------------------------------------------------- RMSNorm
+
+// One workgroup per token: out = x / sqrt(mean(x^2) + eps) * w, with 16-byte accesses (8 bf16 or 4 fp32
+// per chunk).  Sum of squares in fp32: per thread, per wave (shuffles), then across the 4 waves in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void rms_norm_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                       T* __restrict__ out, int D, float eps) {
+  constexpr int V = 16 / sizeof(T);
+  typedef __attribute__((__vector_size__(16))) unsigned u32x4;
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * D;
+  T* orow = out + row * D;
+  const int chunks = D / V;
+  float ss = 0.0f;
+  for (int k = threadIdx.x; k < chunks; k += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + k * V);
+    const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float v = jm::io<T>::cvt(e[i]);
+      ss = fmaf(v, v, ss);
+    }
+  }
+  ss = jm::wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / D + eps);
+  for (int k = threadIdx.x; k < chunks; k += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + k * V);
+    const u32x4 wraw = *reinterpret_cast<const u32x4*>(w + k * V);
+    const T* e = reinterpret_cast<const T*>(&raw);
+    const T* we = reinterpret_cast<const T*>(&wraw);
+    u32x4 o;
+    T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+    for (int i = 0; i < V; ++i) oe[i] = jm::io<T>::from(jm::io<T>::cvt(e[i]) * r * jm::io<T>::cvt(we[i]));
+    *reinterpret_cast<u32x4*>(orow + k * V) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------- GEMMs
+
+// One hipBLASLt handle per device, and the algorithm chosen for each GEMM shape, created on first use.
+struct GemmKey {
+  int dev, dtype;
+  int64_t m, n, k, lda, ldb, ldc, ldd;
+  bool beta;
+  bool operator<(const GemmKey& o) const {
+    return std::tie(dev, dtype, m, n, k, lda, ldb, ldc, ldd, beta) <
+           std::tie(o.dev, o.dtype, o.m, o.n, o.k, o.lda, o.ldb, o.ldc, o.ldd, o.beta);
+  }
+};
+std::mutex g_gemm_mu;
+hipblasLtHandle_t g_handle[kMaxDevices];
+std::map<GemmKey, hipblasLtMatmulAlgo_t> g_algos;
+
+// Row-major Y[T, N] = X[T, K] . W[N, K]^T (+ R[T, N] when res is given), all of the I/O type, fp32
+// accumulation.  In hipBLASLt's column-major terms: D[N, T] = op(A)[N, K] . B[K, T] + C with A = W (its
+// row-major [N, K] is column-major [K, N], transposed), B = X (column-major [K, T]), C = R, D = Y.
+int gemm(bool bf16, const void* X, int64_t ldx, const void* W, int64_t ldw, void* Y, int64_t ldy, const void* res,
+         int64_t ldr, int64_t T, int64_t N, int64_t K, void* ws, hipStream_t st) {
+  if (T == 0) return JM_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return JM_ERR_HIP;
+  const hipDataType ty = bf16 ? HIP_R_16BF : HIP_R_32F;
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr, ld = nullptr;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  int status = JM_ERR_HIP;
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  const uint64_t wsz = kGemmWorkspace;
+  const float alpha = 1.0f, beta = res ? 1.0f : 0.0f;
+  const GemmKey key{dev, bf16 ? 1 : 0, N, T, K, ldw, ldx, res ? ldr : ldy, ldy, res != nullptr};
+  hipblasLtMatmulAlgo_t algo;
+  do {
+    if (hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) break;
+    if (hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) !=
+            HIPBLAS_STATUS_SUCCESS)
+      break;
+    if (hipblasLtMatrixLayoutCreate(&la, ty, K, N, ldw) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&lb, ty, K, T, ldx) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&lc, ty, N, T, res ? ldr : ldy) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&ld, ty, N, T, ldy) != HIPBLAS_STATUS_SUCCESS)
+      break;
+    {
+      std::lock_guard<std::mutex> lock(g_gemm_mu);
+      if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
+        g_handle[dev] = nullptr;
+        break;
+      }
+      auto it = g_algos.find(key);
+      if (it == g_algos.end()) {
+        if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS ||
+            hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz,
+                                                  sizeof(wsz)) != HIPBLAS_STATUS_SUCCESS)
+          break;
+        hipblasLtMatmulHeuristicResult_t heur[1];
+        int found = 0;
+        if (hipblasLtMatmulAlgoGetHeuristic(g_handle[dev], op, la, lb, lc, ld, pref, 1, heur, &found) !=
+                HIPBLAS_STATUS_SUCCESS ||
+            found < 1) {
+          status = JM_ERR_UNSUPPORTED;
+          break;
+        }
+        it = g_algos.emplace(key, heur[0].algo).first;
+      }
+      algo = it->second;
+    }
+    const void* C = res ? res : Y;
+    if (hipblasLtMatmul(g_handle[dev], op, &alpha, W, la, X, lb, &beta, C, lc, Y, ld, &algo, ws, wsz, st) !=
+        HIPBLAS_STATUS_SUCCESS)
+      break;
+    status = JM_OK;
+  } while (false);
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (ld) hipblasLtMatrixLayoutDestroy(ld);
+  if (lc) hipblasLtMatrixLayoutDestroy(lc);
+  if (lb) hipblasLtMatrixLayoutDestroy(lb);
+  if (la) hipblasLtMatrixLayoutDestroy(la);
+  if (op) hipblasLtMatmulDescDestroy(op);
+  return status;
+}
+
+// ---------------------------------------------------------------------------------------------- the layer
+
+struct LayerPlan {
+  jm_mixer_dims md;     // the mixer's dims with x / z strided views of the in_proj output
+  int64_t T, C, Dm, esize;
+  int64_t off_hn, off_xz, off_y, off_mixer, off_gemm, total;
+};
+
+int layer_plan(const jm_layer_dims* d, bool decode, LayerPlan* p) {
+  if (!d) return JM_ERR_INVALID_ARG;
+  if (d->d_model < 1 || !(d->layer_norm_eps >= 0.0f)) return JM_ERR_INVALID_ARG;
+  if (d->d_model % 8 != 0) return JM_ERR_UNSUPPORTED;
+  p->md = d->mixer;
+  p->md.x_row_stride = 2 * (int64_t)d->mixer.d_inner;
+  p->md.z_row_stride = 2 * (int64_t)d->mixer.d_inner;
+  const int64_t mws = jm::mixer_workspace_bytes(&p->md, decode);
+  if (mws < 0) return (int)mws;   // the mixer's own validation code
+  p->T = (int64_t)d->mixer.batch * (decode ? 1 : d->mixer.seqlen);
+  p->C = d->mixer.d_inner;
+  p->Dm = d->d_model;
+  p->esize = d->mixer.io_dtype == JM_BF16 ? 2 : 4;
+  int64_t off = 0;
+  p->off_hn = off;    off += align_up(p->T * p->Dm * p->esize);
+  p->off_xz = off;    off += align_up(p->T * 2 * p->C * p->esize);
+  p->off_y = off;     off += align_up(p->T * p->C * p->esize);
+  p->off_mixer = off; off += align_up(mws);
+  p->off_gemm = off;  off += kGemmWorkspace;
+  p->total = off;
+  return JM_OK;
+}
+
+int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void* x_res, void* out,
+              const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+              void* stream, bool decode) {
+  LayerPlan p;
+  int s = layer_plan(dims, decode, &p);
+  if (s != JM_OK) return s;
+  if (!lw || !lw->norm_w || !lw->in_proj_w || !lw->out_proj_w) return JM_ERR_INVALID_ARG;
+  const void* ptrs[] = {lw->norm_w, lw->in_proj_w, lw->out_proj_w, x_res, out, ws};
+  for (const void* q : ptrs)
+    if (q && ((uintptr_t)q & 15u) != 0) return JM_ERR_ALIGNMENT;
+  if (p.T > 0 && (!x_res || !out)) return JM_ERR_INVALID_ARG;
+  if (!conv_out || !h_out || (decode && (!conv_in || !h0))) return JM_ERR_INVALID_ARG;
+  if (!ws || (int64_t)ws_bytes < p.total) return JM_ERR_WORKSPACE;
+  const bool bf16 = dims->mixer.io_dtype == JM_BF16;
+  char* base = (char*)ws;
+  void* hn = base + p.off_hn;
+  char* xz = base + p.off_xz;
+  void* y = base + p.off_y;
+  void* mws = base + p.off_mixer;
+  void* gws = base + p.off_gemm;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t mws_bytes = (size_t)(p.off_gemm - p.off_mixer);
+  // everything the mixer checks, before the norm and in_proj are enqueued
+  if ((s = jm::mixer_validate(&p.md, &lw->mixer, p.T > 0 ? xz : nullptr, p.T > 0 ? xz + p.C * p.esize : nullptr,
+                              p.T > 0 ? y : nullptr, conv_in, conv_out, h0, h_out, mws, mws_bytes, decode)) != JM_OK)
+    return s;
+  if (p.T == 0) {   // no tokens: the mixer copies the states through
+    return jm::mixer_run(&p.md, &lw->mixer, nullptr, nullptr, nullptr, conv_in, conv_out, h0, h_out, mws,
+                         mws_bytes, stream, decode);
+  }
+  (void)hipGetLastError();
+  if (bf16)
+    hipLaunchKernelGGL(rms_norm_kernel<jm::bf16_t>, dim3((unsigned)p.T), dim3(256), 0, st,
+                       (const jm::bf16_t*)x_res, (const jm::bf16_t*)lw->norm_w, (jm::bf16_t*)hn, (int)p.Dm,
+                       dims->layer_norm_eps);
+  else
+    hipLaunchKernelGGL(rms_norm_kernel<float>, dim3((unsigned)p.T), dim3(256), 0, st, (const float*)x_res,
+                       (const float*)lw->norm_w, (float*)hn, (int)p.Dm, dims->layer_norm_eps);
+  if (hipGetLastError() != hipSuccess) return JM_ERR_HIP;
+  if ((s = gemm(bf16, hn, p.Dm, lw->in_proj_w, p.Dm, xz, 2 * p.C, nullptr, 0, p.T, 2 * p.C, p.Dm, gws, st)) !=
+      JM_OK)
+    return s;
+  if ((s = jm::mixer_run(&p.md, &lw->mixer, xz, xz + p.C * p.esize, y, conv_in, conv_out, h0, h_out, mws,
+                         mws_bytes, stream, decode)) != JM_OK)
+    return s;
+  return gemm(bf16, y, p.C, lw->out_proj_w, p.C, out, p.Dm, x_res, p.Dm, p.T, p.Dm, p.C, gws, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t jm_layer_prefill_workspace_size(const jm_layer_dims* dims) {
+  LayerPlan p;
+  return layer_plan(dims, false, &p) == JM_OK ? (size_t)p.total : 0;
+}
+
+size_t jm_layer_decode_workspace_size(const jm_layer_dims* dims) {
+  LayerPlan p;
+  return layer_plan(dims, true, &p) == JM_OK ? (size_t)p.total : 0;
+}
+
+int jm_layer_prefill(const jm_layer_dims* dims, const jm_layer_weights* weights, const void* x_res, void* out,
+                     const void* conv_state_in, void* conv_state_out, const float* ssm_state_in,
+                     float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_run(dims, weights, x_res, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out,
+                   workspace, workspace_bytes, stream, false);
+}
+
+int jm_layer_decode_step(const jm_layer_dims* dims, const jm_layer_weights* weights, const void* x_res,
+                         void* out, const void* conv_state_in, void* conv_state_out, const float* ssm_state_in,
+                         float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_run(dims, weights, x_res, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out,
+                   workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -140,9 +140,10 @@ struct StageMarks {
   }
 };
 
-int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
-        const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-        void* stream, bool decode, void** events = nullptr, int n_events = 0) {
+// Every check of a call, before anything is enqueued.
+int validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+             const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+             bool decode) {
   int s = check_dims(dims, decode);
   if (s != JM_OK) return s;
   if ((s = check_weights(w)) != JM_OK) return s;
@@ -154,6 +155,15 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return JM_ERR_ALIGNMENT;
   if (!ws || (int64_t)ws_bytes < p.total) return JM_ERR_WORKSPACE;
+  return JM_OK;
+}
+
+int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+        const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+        void* stream, bool decode, void** events = nullptr, int n_events = 0) {
+  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode);
+  if (s != JM_OK) return s;
+  const Plan p = make_plan(dims, decode);
   if (events) {
     if (n_events < JM_STAGES + 1) return JM_ERR_INVALID_ARG;
     for (int i = 0; i <= JM_STAGES; ++i)
@@ -219,6 +229,28 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
 }
 
 }  // namespace
+
+namespace jm {
+
+int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode) {
+  const int s = check_dims(dims, decode);
+  if (s != JM_OK) return s;
+  return make_plan(dims, decode).total;
+}
+
+int mixer_validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+                   const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+                   bool decode) {
+  return validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode);
+}
+
+int mixer_run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
+              const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
+              void* stream, bool decode) {
+  return run(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, stream, decode);
+}
+
+}  // namespace jm
 
 extern "C" {
 

@@ -10,14 +10,15 @@ import pytest
 import mamba_selective_scan_05_amd as jm
 from mamba_selective_scan_05_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jm_mixer.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 FAKE = 0x10000          # 16-byte aligned stand-in pointer; never dereferenced because validation fails first
 WS_BIG = 1 << 40
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(jm_\w+)\s*\(", src, flags=re.M)))
 
@@ -25,7 +26,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"jm_mixer_prefill", "jm_mixer_decode_step", "jm_mixer_prefill_workspace_size",
-            "jm_mixer_decode_workspace_size", "jm_status_string"} <= set(names)
+            "jm_mixer_decode_workspace_size", "jm_status_string", "jm_layer_prefill", "jm_layer_decode_step",
+            "jm_layer_prefill_workspace_size", "jm_layer_decode_workspace_size"} <= set(names)
     L = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -115,3 +117,26 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert len(jm.status_string(s)) >= 2
     assert jm.status_string(-99) == "unknown status"
+
+
+def test_layer_validation_before_launch():
+    # the whole-layer entry points check everything (their own dims and pointers and the mixer's) before
+    # anything is enqueued; with stand-in pointers they must return an error without touching a GPU
+    d = jm.make_layer_dims(2, 64, 128, 16, jm.JM_BF16, 64)
+    n = jm.layer_workspace_size(d)
+    assert n > 0 and jm.layer_workspace_size(d, decode=True) > 0
+    assert jm.layer_workspace_size(jm.make_layer_dims(2, 64, 128, 16, jm.JM_BF16, 60)) == 0      # d_model % 8
+    assert jm.layer_workspace_size(jm.make_layer_dims(2, 64, 96, 16, jm.JM_BF16, 64)) == 0       # d_inner % 64
+    mixer_w = jm.Weights(*([FAKE] * 10))
+    lw = jm.LayerWeights(FAKE, FAKE, FAKE, mixer_w)
+    call = lambda dims, w, x, out, ci, co, hi, ho, ws, nbytes, decode=False: jm.call_layer(
+        dims, w, x, out, ci, co, hi, ho, ws, nbytes, 0, decode)
+    assert call(d, lw, FAKE, FAKE, None, None, None, None, FAKE, WS_BIG) == _lib.JM_ERR_INVALID_ARG   # no outputs
+    assert call(d, lw, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, n - 1) == _lib.JM_ERR_WORKSPACE
+    assert call(d, lw, FAKE + 4, FAKE, None, FAKE, None, FAKE, FAKE, WS_BIG) == _lib.JM_ERR_ALIGNMENT
+    assert call(d, jm.LayerWeights(None, FAKE, FAKE, mixer_w), FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
+                WS_BIG) == _lib.JM_ERR_INVALID_ARG
+    bad_mixer = jm.Weights(*([FAKE] * 9 + [None]))          # D missing: the mixer's own check, still first
+    assert call(d, jm.LayerWeights(FAKE, FAKE, FAKE, bad_mixer), FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
+                WS_BIG) == _lib.JM_ERR_INVALID_ARG
+    assert call(d, lw, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, WS_BIG, decode=True) == _lib.JM_ERR_INVALID_ARG
