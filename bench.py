@@ -293,6 +293,59 @@ def cpu_baseline(cfg, max_tokens):
                       f"C={cfg.d_inner}), {dt:.1f} s; matmuls on {blas} BLAS threads, the scan single-threaded"}
 
 
+def time_layer(jm, cfg, steps, warmup, decode):
+    """The whole Mamba layer (pre-norm, in_proj, mixer, out_proj, residual) on the same synthetic workload;
+    decode rotates the states like the mixer's decode timing."""
+    import torch
+    from jm_inputs import make_layer_input, make_layer_weights, make_state, make_weights
+
+    dev = "cuda"
+    layer = jm.Layer(make_layer_weights(cfg, dev), make_weights(cfg, dev), cfg.dt_rank, cfg.d_state, cfg.d_conv,
+                     cfg.norm_eps, 1e-6)
+    B, C = cfg.batch, cfg.d_inner
+    L = 1 if decode else cfg.seqlen
+    dims = layer.dims(B, L)
+    ws = layer.workspace(jm.layer_workspace_size(dims, decode))
+    stream = torch.cuda.current_stream().cuda_stream
+    if decode:
+        st = make_state(cfg, dev)
+        sets = [(st["conv_state"].clone(), st["ssm_state"].clone()) for _ in range(N_STATE_SETS)]
+        xs = make_layer_input(cfg, dev, steps=8)
+        xin = [xs[:, i].contiguous() for i in range(8)]
+    else:
+        xin = [make_layer_input(cfg, dev)]
+        cs = torch.empty((B, C, cfg.d_conv - 1), dtype=cfg.torch_dtype, device=dev)
+        hs = torch.empty((B, C, cfg.d_state), dtype=torch.float32, device=dev)
+    out = torch.empty_like(xin[0])
+
+    def step(i):
+        if decode:
+            c, h = sets[i % N_STATE_SETS]
+            ptrs = (c.data_ptr(), c.data_ptr(), h.data_ptr(), h.data_ptr())
+        else:
+            ptrs = (None, cs.data_ptr(), None, hs.data_ptr())
+        s = jm.call_layer(dims, layer.packed, xin[i % len(xin)].data_ptr(), out.data_ptr(), *ptrs, ws.data_ptr(),
+                          ws.numel(), stream, decode)
+        if s != 0:
+            raise jm.JMError(s, "jm_layer_decode_step" if decode else "jm_layer_prefill")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    Dm = cfg.d_model
+    gemm_flops = 2.0 * B * L * Dm * (2 * C) + 2.0 * B * L * C * Dm
+    return {"workload": f"{cfg.name}: whole Mamba layer (RMSNorm, in_proj, mixer, out_proj, residual)",
+            "batch": B, "seq_len": L, "d_model": Dm, "us_per_step": round(ms * 1e3, 2),
+            "tokens_per_s": round(B * L / (ms * 1e-3), 1), "gemm_flops_per_step": gemm_flops}
+
+
 def run_decode(jm, dcfg, args, hip):
     log(f"decode {dcfg.name}: warmup {args.warmup}, steps {args.steps}")
     dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
@@ -318,6 +371,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--config", type=int, default=1, choices=(1, 2, 3),
                     help="prefill workload: 1 = B1 L4096 (default), 2 = B8 L4096, 3 = B1 L262144")
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workload and print its figures (for per-workload profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -406,6 +460,23 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = run_decode(jm, CONFIGS[4], args, hip)
+    if not args.no_layer and args.config == 1:
+        from jm_inputs import LAYER_CONFIGS
+        lay = {}
+        for name, lcfg, dec in (("prefill", LAYER_CONFIGS[0], False), ("decode", LAYER_CONFIGS[1], True)):
+            log(f"layer {lcfg.name}: warmup {args.warmup}, steps {args.steps}")
+            lay[name] = time_layer(jm, lcfg, args.steps, args.warmup, dec)
+            # the mixer's share of the step, from the mixer-only timings above (prefill) or the decode entry
+            mix_us = pre["ms"] * 1e3 if name == "prefill" else result.get("decode", {}).get("us_per_step")
+            if mix_us:
+                rest = lay[name]["us_per_step"] - mix_us
+                lay[name]["mixer_us"] = round(mix_us, 2)
+                if rest > 0:
+                    lay[name]["gemm_norm_us"] = round(rest, 2)
+                    tflops = lay[name]["gemm_flops_per_step"] / (rest * 1e-6) / 1e12
+                    lay[name]["gemm_tflops_estimate"] = round(tflops, 1)
+            log(f"  {name}: {lay[name]['us_per_step']:.1f} us per step")
+        result["layer"] = lay
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {min(args.cpu_tokens, cfg.seqlen)} tokens ...")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
