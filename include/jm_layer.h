@@ -75,6 +75,16 @@ int jm_layer_decode_step(const jm_layer_dims* dims, const jm_layer_weights* weig
                          const float* ssm_state_in, float* ssm_state_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode step over pools of per-sequence states (serving): jm_layer_decode_step with sequence b's states in
+ * row slots[b] of conv_state_pool [pool_size, C, K-1] and ssm_state_pool [pool_size, C, N] float32, updated
+ * in place, exactly as in jm_mixer_decode_step_slots (slots: device int32 [batch]; valid entries distinct;
+ * an entry outside [0, pool_size) runs from zero states and stores none).
+ */
+int jm_layer_decode_step_slots(const jm_layer_dims* dims, const jm_layer_weights* weights, const void* x_res,
+                               void* out, void* conv_state_pool, float* ssm_state_pool, int32_t pool_size,
+                               const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

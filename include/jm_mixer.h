@@ -148,6 +148,30 @@ int jm_mixer_decode_step(const jm_mixer_dims* dims, const jm_mixer_weights* weig
                          const float* ssm_state_in, float* ssm_state_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode step over a pool of per-sequence states: the decode step above, with sequence b's conv and SSM
+ * states kept in row slots[b] of two state pools that the step updates in place.  This is the state
+ * layout of a serving engine that batches whichever sequences are generating at the moment (Jamba Guide,
+ * aifetchly blog, "Production Engineering: Serving & Hardware Best Practices": serving with continuous
+ * batching; TransformerLens "supported_architectures.jamba": generation carries the Mamba conv and
+ * recurrent states in a cache), so that a batch can be formed without gathering and scattering states.
+ *   x, z, out         as in jm_mixer_decode_step ([batch, row_stride] in, [batch, C] out)
+ *   conv_state_pool   in/out [pool_size, C, K-1] in io_dtype
+ *   ssm_state_pool    in/out [pool_size, C, N] float32
+ *   pool_size         rows in each pool (>= 1)
+ *   slots             DEVICE int32 [batch], 4-byte aligned: the pool row of each sequence.  The valid
+ *                     entries must be distinct (two sequences on one row race).  An entry outside
+ *                     [0, pool_size) — e.g. -1 for a padding entry of the batch — runs from zero states,
+ *                     writes its out row and stores no state; it is not an error (the host does not read
+ *                     the device's slot values).
+ *   workspace         scratch of at least jm_mixer_decode_workspace_size(dims) bytes.
+ * Rows of the pools that no valid slot names are left untouched.
+ */
+int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights* weights,
+                               const void* x, const void* z, void* out,
+                               void* conv_state_pool, float* ssm_state_pool, int32_t pool_size,
+                               const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* jm_status_string(int status);
 

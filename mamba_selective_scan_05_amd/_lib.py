@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, V, V, V, S, V]
             f.restype = I
+        L.jm_mixer_decode_step_slots.argtypes = [P(Dims), P(Weights), V, V, V, V, V, ctypes.c_int32, V, V, S, V]
+        L.jm_mixer_decode_step_slots.restype = I
+        L.jm_layer_decode_step_slots.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, ctypes.c_int32, V, V,
+                                                 S, V]
+        L.jm_layer_decode_step_slots.restype = I
         for name in ("jm_layer_prefill_workspace_size", "jm_layer_decode_workspace_size"):
             f = getattr(L, name)
             f.argtypes = [P(LayerDims)]
@@ -149,6 +154,22 @@ def call_decode_step(dims: Dims, weights: Weights, x, z, out, conv_in, conv_out,
                      stream: int) -> int:
     return lib().jm_mixer_decode_step(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in, h_out, ws,
                                       ws_bytes, stream)
+
+
+def call_decode_step_slots(dims: Dims, weights: Weights, x, z, out, conv_pool, ssm_pool, pool_size: int, slots,
+                           ws, ws_bytes: int, stream: int) -> int:
+    """The raw state-pool decode entry point on integer device pointers (None for NULL)."""
+    return lib().jm_mixer_decode_step_slots(_ref(dims), _ref(weights), x, z, out, conv_pool, ssm_pool, pool_size,
+                                            slots, ws, ws_bytes, stream)
+
+
+def _check_pools(conv_pool: torch.Tensor, ssm_pool: torch.Tensor, slots: torch.Tensor, batch: int) -> int:
+    if slots.dtype != torch.int32 or slots.dim() != 1 or slots.shape[0] != batch or not slots.is_contiguous():
+        raise ValueError(f"slots must be a contiguous int32 vector of length {batch}")
+    if conv_pool.shape[0] != ssm_pool.shape[0]:
+        raise ValueError("conv and SSM state pools differ in rows")
+    _check_contiguous(conv_pool=conv_pool, ssm_pool=ssm_pool)
+    return int(conv_pool.shape[0])
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -255,6 +276,26 @@ class Mixer:
             raise JMError(s, "jm_mixer_decode_step")
         return out, conv_state_out, ssm_state_out
 
+    def decode_step_slots(self, x: torch.Tensor, z: torch.Tensor, conv_pool: torch.Tensor, ssm_pool: torch.Tensor,
+                          slots: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """One token per sequence with the states in pools ([P, C, K-1] and [P, C, N]) updated in place at
+        rows slots[b] (a device int32 [B]; an entry outside [0, P) runs from zero states and stores none)."""
+        B, C = x.shape
+        pool = _check_pools(conv_pool, ssm_pool, slots, B)
+        dims = self.dims(B, 1, _row_stride(x, 1), _row_stride(z, 1))
+        nbytes = decode_workspace_size(dims)
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_mixer_decode_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.empty((B, C), dtype=self.dtype, device=self.device)
+        _check_contiguous(out=out)
+        s = call_decode_step_slots(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_pool), _ptr(ssm_pool),
+                                   pool, _ptr(slots), _ptr(ws), ws.numel(), _stream(self.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_mixer_decode_step_slots")
+        return out
+
 
 def make_layer_dims(batch: int, seqlen: int, d_inner: int, dt_rank: int, io_dtype: int, d_model: int,
                     d_state: int = 16, d_conv: int = 4, norm_eps: float = 1e-6,
@@ -335,3 +376,23 @@ class Layer:
         """x_res [B, d_model]; with in_place=True the states are updated in place."""
         co, so = (conv_state, ssm_state) if in_place else (None, None)
         return self._run(x_res, conv_state, ssm_state, out, co, so, True)
+
+    def decode_step_slots(self, x_res: torch.Tensor, conv_pool: torch.Tensor, ssm_pool: torch.Tensor,
+                          slots: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """x_res [B, d_model]; the states live in pools updated in place at rows slots[b] (device int32 [B])."""
+        B = x_res.shape[0]
+        pool = _check_pools(conv_pool, ssm_pool, slots, B)
+        dims = self.dims(B, 1)
+        nbytes = layer_workspace_size(dims, True)
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_layer_decode_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.empty_like(x_res)
+        _check_contiguous(x_res=x_res, out=out)
+        s = lib().jm_layer_decode_step_slots(_ref(dims), _ref(self.packed), _ptr(x_res), _ptr(out), _ptr(conv_pool),
+                                             _ptr(ssm_pool), pool, _ptr(slots), _ptr(ws), ws.numel(),
+                                             _stream(self.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_layer_decode_step_slots")
+        return out

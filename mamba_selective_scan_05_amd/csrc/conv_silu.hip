@@ -156,7 +156,7 @@ template <typename T, int SPB>
 __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x, int64_t xs,
                                                         const T* __restrict__ conv_w, const T* __restrict__ conv_b,
                                                         const T* conv_in, T* __restrict__ xc, T* conv_out, int B,
-                                                        int C) {
+                                                        int C, const int32_t* __restrict__ slots, int pool) {
   constexpr int V = Vec16<T>::n;
   constexpr int S3 = kTaps - 1;
   __shared__ uint4 sst[256 * S3], sw[256 * kTaps];
@@ -185,11 +185,19 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x,
   // sequence s: state chunks tid, tid + 256, tid + 512 (clamped to the block; zeros without a state) and the
   // thread's 16 bytes of input
   uint4 rs[S3], rx;
+  // the state row of sequence b: b itself, or its slot in the pool (-1: none, a zero state stored nowhere)
+  auto state_row = [&](int64_t b) -> int64_t {
+    if (!slots) return b;
+    const int s = slots[b];
+    return s >= 0 && s < pool ? s : -1;
+  };
   auto load_seq = [&](int s) {
     const int64_t b = b0 + s;
-    const uint4* gst = reinterpret_cast<const uint4*>(conv_in + (b * C + cbase) * S3);
+    const int64_t row = state_row(b);
+    const uint4* gst = reinterpret_cast<const uint4*>(conv_in + (max(row, (int64_t)0) * C + cbase) * S3);
 #pragma unroll
-    for (int q = 0; q < S3; ++q) rs[q] = conv_in ? gst[min(tid + 256 * q, ng * S3 - 1)] : make_uint4(0u, 0u, 0u, 0u);
+    for (int q = 0; q < S3; ++q)
+      rs[q] = conv_in && row >= 0 ? gst[min(tid + 256 * q, ng * S3 - 1)] : make_uint4(0u, 0u, 0u, 0u);
     rx = *reinterpret_cast<const uint4*>(x + b * xs + cbase + own * V);
   };
   load_seq(0);
@@ -226,7 +234,9 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x,
       for (int q = 0; q < S3; ++q) store16(reinterpret_cast<T*>(&sst[tid * S3 + q]), ns + q * V);
     }
     __syncthreads();
-    uint4* gout = reinterpret_cast<uint4*>(conv_out + (b * C + cbase) * S3);
+    const int64_t row = state_row(b);
+    if (row < 0) continue;
+    uint4* gout = reinterpret_cast<uint4*>(conv_out + (row * C + cbase) * S3);
 #pragma unroll
     for (int q = 0; q < S3; ++q)
       if (tid + 256 * q < ng * S3) gout[tid + 256 * q] = sst[tid + 256 * q];
@@ -266,18 +276,19 @@ void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, 
 }
 
 void launch_conv_step(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
-                      const void* conv_in, void* xc, void* conv_out, int B, int C, hipStream_t st) {
+                      const void* conv_in, void* xc, void* conv_out, int B, int C, hipStream_t st,
+                      const int32_t* slots, int pool) {
   constexpr int kSeqPerBlock = 1;   // measured at B = 256: 7.1 us, against 7.8 (2) and 9.5 (4): parallelism wins
   const int V = bf16 ? 8 : 4;
   dim3 grid((C / V + 255) / 256, (B + kSeqPerBlock - 1) / kSeqPerBlock);
   if (bf16)
     hipLaunchKernelGGL((conv_step_kernel<bf16_t, kSeqPerBlock>), grid, dim3(256), 0, st, (const bf16_t*)x, xs,
                        (const bf16_t*)conv_w, (const bf16_t*)conv_b, (const bf16_t*)conv_in, (bf16_t*)xc,
-                       (bf16_t*)conv_out, B, C);
+                       (bf16_t*)conv_out, B, C, slots, pool);
   else
     hipLaunchKernelGGL((conv_step_kernel<float, kSeqPerBlock>), grid, dim3(256), 0, st, (const float*)x, xs,
                        (const float*)conv_w, (const float*)conv_b, (const float*)conv_in, (float*)xc,
-                       (float*)conv_out, B, C);
+                       (float*)conv_out, B, C, slots, pool);
 }
 
 void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,

@@ -13,9 +13,12 @@ void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* co
                       const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
 
 // One token per sequence (seqlen 1): the same conv + SiLU -> xc [B, C], and the shifted conv state ->
-// conv_state_out [B, C, K-1] (may alias conv_state_in; zeros stand in for a NULL conv_state_in).
+// conv_state_out [B, C, K-1] (may alias conv_state_in; zeros stand in for a NULL conv_state_in).  With
+// slots, sequence b's conv state is row slots[b] of pools of `pool` rows; a slot outside [0, pool) runs
+// from a zero state and stores none.
 void launch_conv_step(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
-                      const void* conv_state_in, void* xc, void* conv_state_out, int B, int C, hipStream_t st);
+                      const void* conv_state_in, void* xc, void* conv_state_out, int B, int C, hipStream_t st,
+                      const int32_t* slots = nullptr, int pool = 0);
 
 // Tokens per x_proj workgroup tile (bf16 path), and the number of column groups (grid z) for N columns in
 // the wide (288 columns per workgroup) or narrow (32) layout.
@@ -54,6 +57,10 @@ struct ScanArgs {
   float* loc;            // [B, P, N+1, C]   per-piece local end states and dt sums (P > 1)
   float* cin;            // [B, P, N, C]     per-piece incoming states (P > 1)
   int B, L, C, P, Lp;
+  // Decode with a state pool (P = 1): sequence b's SSM state is row slots[b] of h0 / h_out (pools of `pool`
+  // rows); a slot outside [0, pool) runs from a zero state and stores nothing.  Null: row b.
+  const int32_t* slots;
+  int pool;
 };
 
 // The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.
@@ -64,12 +71,14 @@ void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* mark
 // of a call (a negative jm_status for invalid dims), every check of a call without launching anything, and
 // the validated call itself (each a jm_status).
 int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode);
+// With slots (decode only), the states are pools of `pool` rows indexed by slots[b], as in
+// jm_mixer_decode_step_slots.
 int mixer_validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
                    const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-                   bool decode);
+                   bool decode, const int32_t* slots = nullptr, int pool = 0);
 int mixer_run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
               const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-              void* stream, bool decode);
+              void* stream, bool decode, const int32_t* slots = nullptr, int pool = 0);
 
 // seqlen == 0: copy the states through (zeros for a NULL input).
 void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,

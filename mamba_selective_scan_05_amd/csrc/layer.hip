@@ -180,7 +180,7 @@ int layer_plan(const jm_layer_dims* d, bool decode, LayerPlan* p) {
 
 int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void* x_res, void* out,
               const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-              void* stream, bool decode) {
+              void* stream, bool decode, const int32_t* slots = nullptr, int pool = 0) {
   LayerPlan p;
   int s = layer_plan(dims, decode, &p);
   if (s != JM_OK) return s;
@@ -202,7 +202,8 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
   const size_t mws_bytes = (size_t)(p.off_gemm - p.off_mixer);
   // everything the mixer checks, before the norm and in_proj are enqueued
   if ((s = jm::mixer_validate(&p.md, &lw->mixer, p.T > 0 ? xz : nullptr, p.T > 0 ? xz + p.C * p.esize : nullptr,
-                              p.T > 0 ? y : nullptr, conv_in, conv_out, h0, h_out, mws, mws_bytes, decode)) != JM_OK)
+                              p.T > 0 ? y : nullptr, conv_in, conv_out, h0, h_out, mws, mws_bytes, decode, slots,
+                              pool)) != JM_OK)
     return s;
   if (p.T == 0) {   // no tokens: the mixer copies the states through
     return jm::mixer_run(&p.md, &lw->mixer, nullptr, nullptr, nullptr, conv_in, conv_out, h0, h_out, mws,
@@ -221,7 +222,7 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
       JM_OK)
     return s;
   if ((s = jm::mixer_run(&p.md, &lw->mixer, xz, xz + p.C * p.esize, y, conv_in, conv_out, h0, h_out, mws,
-                         mws_bytes, stream, decode)) != JM_OK)
+                         mws_bytes, stream, decode, slots, pool)) != JM_OK)
     return s;
   return gemm(bf16, y, p.C, lw->out_proj_w, p.C, out, p.Dm, x_res, p.Dm, p.T, p.Dm, p.C, gws, st);
 }
@@ -252,6 +253,14 @@ int jm_layer_decode_step(const jm_layer_dims* dims, const jm_layer_weights* weig
                          float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
   return layer_run(dims, weights, x_res, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out,
                    workspace, workspace_bytes, stream, true);
+}
+
+int jm_layer_decode_step_slots(const jm_layer_dims* dims, const jm_layer_weights* weights, const void* x_res,
+                               void* out, void* conv_state_pool, float* ssm_state_pool, int32_t pool_size,
+                               const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!slots) return JM_ERR_INVALID_ARG;
+  return layer_run(dims, weights, x_res, out, conv_state_pool, conv_state_pool, ssm_state_pool, ssm_state_pool,
+                   workspace, workspace_bytes, stream, true, slots, pool_size);
 }
 
 }  // extern "C"

@@ -143,13 +143,17 @@ struct StageMarks {
 // Every check of a call, before anything is enqueued.
 int validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
              const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-             bool decode) {
+             bool decode, const int32_t* slots = nullptr, int pool = 0) {
   int s = check_dims(dims, decode);
   if (s != JM_OK) return s;
   if ((s = check_weights(w)) != JM_OK) return s;
   const Plan p = make_plan(dims, decode);
   if (!conv_out || !h_out) return JM_ERR_INVALID_ARG;
   if (decode && (!conv_in || !h0)) return JM_ERR_INVALID_ARG;
+  if (slots) {   // a state pool: decode only, at least one row, int32 indices
+    if (!decode || pool < 1) return JM_ERR_INVALID_ARG;
+    if (((uintptr_t)slots & 3u) != 0) return JM_ERR_ALIGNMENT;
+  }
   if (p.L > 0 && (!x || !z || !out)) return JM_ERR_INVALID_ARG;
   const void* ptrs[] = {x, z, out, conv_in, conv_out, h0, h_out, ws};
   for (const void* q : ptrs)
@@ -160,8 +164,9 @@ int validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x
 
 int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
         const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-        void* stream, bool decode, void** events = nullptr, int n_events = 0) {
-  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode);
+        void* stream, bool decode, void** events = nullptr, int n_events = 0, const int32_t* slots = nullptr,
+        int pool = 0) {
+  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool);
   if (s != JM_OK) return s;
   const Plan p = make_plan(dims, decode);
   if (events) {
@@ -190,7 +195,8 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   // one token per sequence: the single-step conv also writes the conv state, so the scan skips it
   const bool step = p.L == 1;
   if (step)
-    jm::launch_conv_step(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, conv_out, p.B, p.C, st);
+    jm::launch_conv_step(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, conv_out, p.B, p.C, st, slots,
+                         pool);
   else
     jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st);
   marks.mark(1);
@@ -222,6 +228,8 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.C = p.C;
   a.P = p.P;
   a.Lp = p.Lp;
+  a.slots = slots;
+  a.pool = pool;
   // the scan records events[4] (local pass), events[5] (carry pass) and events[6] (full pass)
   jm::launch_scan(p.bf16, a, st, events ? &marks.ev[4] : nullptr);
   marks.mark(JM_STAGES);
@@ -240,14 +248,15 @@ int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode) {
 
 int mixer_validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
                    const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-                   bool decode) {
-  return validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode);
+                   bool decode, const int32_t* slots, int pool) {
+  return validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool);
 }
 
 int mixer_run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
               const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-              void* stream, bool decode) {
-  return run(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, stream, decode);
+              void* stream, bool decode, const int32_t* slots, int pool) {
+  return run(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, stream, decode, nullptr, 0, slots,
+             pool);
 }
 
 }  // namespace jm
@@ -276,6 +285,15 @@ int jm_mixer_decode_step(const jm_mixer_dims* dims, const jm_mixer_weights* weig
                          float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
   return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
              workspace_bytes, stream, true);
+}
+
+int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
+                               const void* z, void* out, void* conv_state_pool, float* ssm_state_pool,
+                               int32_t pool_size, const int32_t* slots, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!slots) return JM_ERR_INVALID_ARG;
+  return run(dims, weights, x, z, out, conv_state_pool, conv_state_pool, ssm_state_pool, ssm_state_pool,
+             workspace, workspace_bytes, stream, true, nullptr, 0, slots, pool_size);
 }
 
 int jm_mixer_prefill_profiled(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,

@@ -118,12 +118,18 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float hs[64 * kN];
   float a2[kN], h[kN];
   load_a2((const T*)a.A_log, c, a2);
+  // the SSM state row of sequence b: b itself, or its slot in a state pool (-1: none)
+  int64_t srow = b;
+  if (a.slots) {
+    const int s = a.slots[b];
+    srow = s >= 0 && s < a.pool ? s : -1;
+  }
   if (FULL && P > 1) {
     const float* src = a.cin + ((int64_t)b * P + p) * kN * C + c;
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = src[(int64_t)n * C];
-  } else if (p == 0 && a.h0) {
-    state_load(a.h0 + ((int64_t)b * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+  } else if (p == 0 && a.h0 && srow >= 0) {
+    state_load(a.h0 + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
   } else {
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
@@ -280,7 +286,8 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     return;
   }
   if (p == P - 1) {
-    state_store(a.h_out + ((int64_t)b * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+    if (srow < 0) return;
+    state_store(a.h_out + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
     // conv state (unless the conv step wrote it): the last K-1 entries of the extended input (old state
     // entries when L < K-1).  All three are read before any is written, so conv_out may alias conv_in.
     if (!a.conv_out) return;

@@ -140,3 +140,28 @@ def test_layer_validation_before_launch():
     assert call(d, jm.LayerWeights(FAKE, FAKE, FAKE, bad_mixer), FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
                 WS_BIG) == _lib.JM_ERR_INVALID_ARG
     assert call(d, lw, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, WS_BIG, decode=True) == _lib.JM_ERR_INVALID_ARG
+
+
+def test_state_pool_decode_validation_before_launch():
+    # the state-pool decode entry points check their slot arguments on the host before anything is enqueued
+    d = _dims(batch=3)
+    w = _weights()
+    call = lambda pool, slots, ws_bytes=WS_BIG: jm.call_decode_step_slots(d, w, FAKE, FAKE, FAKE, FAKE, FAKE, pool,
+                                                                          slots, FAKE, ws_bytes, 0)
+    assert call(4, None) == _lib.JM_ERR_INVALID_ARG            # no slot vector
+    assert call(0, FAKE) == _lib.JM_ERR_INVALID_ARG            # empty pool
+    assert call(-3, FAKE) == _lib.JM_ERR_INVALID_ARG
+    assert call(4, FAKE + 2) == _lib.JM_ERR_ALIGNMENT          # int32 indices need 4-byte alignment
+    assert call(4, FAKE, ws_bytes=16) == _lib.JM_ERR_WORKSPACE  # the slot arguments were accepted
+    assert jm.call_decode_step_slots(d, w, FAKE, FAKE, FAKE, None, FAKE, 4, FAKE, FAKE, WS_BIG, 0) == \
+        _lib.JM_ERR_INVALID_ARG                                  # no conv state pool
+    mixer_w = jm.Weights(*([FAKE] * 10))
+    lw = jm.LayerWeights(FAKE, FAKE, FAKE, mixer_w)
+    ld = jm.make_layer_dims(3, 1, 128, 16, jm.JM_BF16, 64)
+    L = _lib.lib()
+    lcall = lambda pool, slots, ws_bytes=WS_BIG: L.jm_layer_decode_step_slots(
+        ctypes.byref(ld), ctypes.byref(lw), FAKE, FAKE, FAKE, FAKE, pool, slots, FAKE, ws_bytes, None)
+    assert lcall(4, None) == _lib.JM_ERR_INVALID_ARG
+    assert lcall(0, FAKE) == _lib.JM_ERR_INVALID_ARG
+    assert lcall(4, FAKE + 2) == _lib.JM_ERR_ALIGNMENT
+    assert lcall(4, FAKE, ws_bytes=16) == _lib.JM_ERR_WORKSPACE

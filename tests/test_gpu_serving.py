@@ -1,0 +1,160 @@
+"""GPU parity of the serving-style entry points: decode over pools of per-sequence states
+(jm_mixer_decode_step_slots, jm_layer_decode_step_slots), through the C ABI.
+
+A serving engine batches whichever sequences are generating and keeps their conv / SSM states in pools;
+the step reads and writes row slots[b] in place.  Checked here, over several steps with the pool carried
+between them:
+  - out and the updated rows against the fp64 oracle run on the gathered states (zeros for an entry
+    outside the pool), to the mixer's tolerances; the conv state rows bit for bit (mixer level);
+  - the same step through the plain decode entry point on gathered copies of the states gives bitwise the
+    same out and states (the two share their kernels);
+  - rows no valid slot names, and every row an out-of-range entry would have touched, stay bitwise
+    unchanged.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jm_inputs import MixerConfig, make_decode_tokens, make_layer_input, make_layer_weights, make_state, \
+    make_weights, to_f64
+from parity_util import assert_bitwise, assert_close, log, weights_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mamba_selective_scan_05_amd as jm
+    jm.lib()
+
+
+def _pool_cfg(name, pool, C, R, io, seed, d_model=0):
+    # the pool's states come from make_state with batch = pool rows
+    return MixerConfig(name, batch=pool, seqlen=1, d_inner=C, dt_rank=R, io_dtype=io, seed=seed, with_state=True,
+                       d_model=d_model, decode_steps=3)
+
+
+def _gather(pool64, slots, P):
+    rows = [pool64[s] if 0 <= s < P else np.zeros_like(pool64[0]) for s in slots]
+    return np.stack(rows)
+
+
+def _scatter(pool64, slots, P, rows):
+    for i, s in enumerate(slots):
+        if 0 <= s < P:
+            pool64[s] = rows[i]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mixer_decode_slots(io):
+    import mamba_selective_scan_05_amd as jm
+    P, C, R = 7, 256, 16
+    slots = [5, 1, -1, 3, 7]          # -1 and 7 (== pool size) are outside the pool
+    B = len(slots)
+    pcfg = _pool_cfg(f"slots_{io}", P, C, R, io, 41)
+    tcfg = pcfg.replace(batch=B)
+    w = make_weights(pcfg, DEV)
+    st = make_state(pcfg, DEV)
+    tok = make_decode_tokens(tcfg, DEV)
+    m = jm.Mixer(w, R, pcfg.d_state, pcfg.d_conv, pcfg.norm_eps)
+    conv_pool, ssm_pool = st["conv_state"].clone(), st["ssm_state"].clone()
+    conv0, ssm0 = conv_pool.clone(), ssm_pool.clone()
+    sl = torch.tensor(slots, dtype=torch.int32, device=DEV)
+    c64, h64 = to_f64(conv_pool), to_f64(ssm_pool)
+    w64 = weights_f64(w)
+    log(f"[slots_{io}] pool={P} slots={slots} C={C} R={R} steps={tcfg.decode_steps}")
+    for t in range(tcfg.decode_steps):
+        x, z = tok["x"][:, t].contiguous(), tok["z"][:, t].contiguous()
+        # the plain entry point on gathered copies of the states (zero states for the out-of-range entries)
+        idx = torch.tensor([s if 0 <= s < P else 0 for s in slots], device=DEV)
+        valid = torch.tensor([0 <= s < P for s in slots], device=DEV)
+        gc = torch.where(valid[:, None, None], conv_pool[idx], torch.zeros_like(conv_pool[idx]))
+        gh = torch.where(valid[:, None, None], ssm_pool[idx], torch.zeros_like(ssm_pool[idx]))
+        ref_out, ref_c, ref_h = m.decode_step(x, z, gc, gh)
+        out = m.decode_step_slots(x, z, conv_pool, ssm_pool, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"step {t}: out differs from the plain decode step"
+        for i, s in enumerate(slots):
+            if 0 <= s < P:
+                assert torch.equal(conv_pool[s], ref_c[i]) and torch.equal(ssm_pool[s], ref_h[i]), (t, s)
+        ro, rc, rh = oracle.mixer_decode_step(to_f64(x), to_f64(z), w64, R, pcfg.d_state, _gather(c64, slots, P),
+                                              _gather(h64, slots, P), pcfg.norm_eps)
+        _scatter(c64, slots, P, rc)
+        _scatter(h64, slots, P, rh)
+        assert_close(f"out[{t}]", out, ro, io)
+    assert_close("ssm pool", ssm_pool, h64, io)
+    assert_bitwise("conv pool", conv_pool, torch.from_numpy(c64).to(pcfg.torch_dtype))
+    for r in (0, 2, 4, 6):            # rows no valid slot names
+        assert torch.equal(conv_pool[r], conv0[r]) and torch.equal(ssm_pool[r], ssm0[r]), r
+
+
+def test_mixer_decode_slots_permuted_full_pool_matches_plain():
+    # every row used, in a scrambled order, at a decode-sized batch (the 32-column x_proj groups)
+    import mamba_selective_scan_05_amd as jm
+    P, C, R = 64, 512, 32
+    cfg = _pool_cfg("slots_perm", P, C, R, "bf16", 42)
+    w = make_weights(cfg, DEV)
+    st = make_state(cfg, DEV)
+    tok = make_decode_tokens(cfg, DEV)
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(42))
+    sl = perm.to(torch.int32).to(DEV)
+    m = jm.Mixer(w, R, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    conv_pool, ssm_pool = st["conv_state"].clone(), st["ssm_state"].clone()
+    cs, hs = st["conv_state"][perm.to(DEV)].clone(), st["ssm_state"][perm.to(DEV)].clone()
+    log(f"[slots_perm] pool={P} C={C} R={R}")
+    for t in range(cfg.decode_steps):
+        x, z = tok["x"][:, t].contiguous(), tok["z"][:, t].contiguous()
+        o1 = m.decode_step_slots(x, z, conv_pool, ssm_pool, sl)
+        o2, _, _ = m.decode_step(x, z, cs, hs, in_place=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), t
+    inv = torch.argsort(perm).to(DEV)
+    assert torch.equal(conv_pool, cs[inv]) and torch.equal(ssm_pool, hs[inv])
+
+
+def test_layer_decode_slots():
+    import mamba_selective_scan_05_amd as jm
+    P, C, R, Dm = 6, 128, 16, 64
+    slots = [4, -1, 0, 2]
+    B = len(slots)
+    pcfg = _pool_cfg("layer_slots", P, C, R, "bf16", 43, d_model=Dm)
+    tcfg = pcfg.replace(batch=B)
+    w = make_weights(pcfg, DEV)
+    lw = make_layer_weights(pcfg, DEV)
+    st = make_state(pcfg, DEV)
+    xs = make_layer_input(tcfg, DEV, steps=3)
+    layer = jm.Layer(lw, w, R, pcfg.d_state, pcfg.d_conv, pcfg.norm_eps, 1e-6)
+    conv_pool, ssm_pool = st["conv_state"].clone(), st["ssm_state"].clone()
+    conv0, ssm0 = conv_pool.clone(), ssm_pool.clone()
+    sl = torch.tensor(slots, dtype=torch.int32, device=DEV)
+    c64, h64 = to_f64(conv_pool), to_f64(ssm_pool)
+    w64, lw64 = weights_f64(w), weights_f64(lw)
+    log(f"[layer_slots] pool={P} slots={slots} C={C} d_model={Dm}")
+    for t in range(xs.shape[1]):
+        x = xs[:, t].contiguous()
+        idx = torch.tensor([s if s >= 0 else 0 for s in slots], device=DEV)
+        valid = torch.tensor([s >= 0 for s in slots], device=DEV)
+        gc = torch.where(valid[:, None, None], conv_pool[idx], torch.zeros_like(conv_pool[idx]))
+        gh = torch.where(valid[:, None, None], ssm_pool[idx], torch.zeros_like(ssm_pool[idx]))
+        ref_out, ref_c, ref_h = layer.decode_step(x, gc, gh)
+        out = layer.decode_step_slots(x, conv_pool, ssm_pool, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), t
+        for i, s in enumerate(slots):
+            if s >= 0:
+                assert torch.equal(conv_pool[s], ref_c[i]) and torch.equal(ssm_pool[s], ref_h[i]), (t, s)
+        ro, rc, rh = oracle.layer_decode_step(to_f64(x), lw64, w64, R, pcfg.d_state, _gather(c64, slots, P),
+                                              _gather(h64, slots, P), pcfg.norm_eps, 1e-6)
+        _scatter(c64, slots, P, rc)
+        _scatter(h64, slots, P, rh)
+        assert_close(f"out[{t}]", out, ro, "bf16")
+    assert_close("ssm pool", ssm_pool, h64, "bf16")
+    assert_close("conv pool", conv_pool, c64, "bf16")
+    for r in (1, 3, 5):
+        assert torch.equal(conv_pool[r], conv0[r]) and torch.equal(ssm_pool[r], ssm0[r]), r
