@@ -85,6 +85,19 @@ int jm_layer_decode_step_slots(const jm_layer_dims* dims, const jm_layer_weights
                                void* out, void* conv_state_pool, float* ssm_state_pool, int32_t pool_size,
                                const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Prefill of a packed batch of variable-length sequences (continuous batching): the layer over
+ * x_res [seqlen, d_model] holding dims->mixer.batch sequences back to back (dims->mixer.seqlen tokens in
+ * all), split by the device offsets cu_seqlens [batch + 1], with states per sequence (or in pools through
+ * slots), exactly as in jm_mixer_prefill_varlen.  out [seqlen, d_model] may be x_res itself.  The
+ * workspace holds at least jm_layer_prefill_varlen_workspace_size(dims) bytes.
+ */
+size_t jm_layer_prefill_varlen_workspace_size(const jm_layer_dims* dims);
+int jm_layer_prefill_varlen(const jm_layer_dims* dims, const jm_layer_weights* weights, const void* x_res,
+                            void* out, const int32_t* cu_seqlens, const void* conv_state_in, void* conv_state_out,
+                            const float* ssm_state_in, float* ssm_state_out, const int32_t* slots,
+                            int32_t pool_size, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

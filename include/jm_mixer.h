@@ -47,8 +47,9 @@
  *      A_log [C, N], D [C] — all contiguous, in io_dtype.
  *  - Requirements (else an error is returned and nothing is enqueued or written):
  *      d_state == 16, d_conv == 4, d_inner a positive multiple of 64, 1 <= dt_rank <= 512 with
- *      dt_rank % 8 == 0, batch >= 1, seqlen >= 0, row strides >= d_inner and multiples of 8 elements,
- *      every pointer 16-byte aligned, norm_eps >= 0.
+ *      dt_rank % 8 == 0, batch >= 1, 0 <= seqlen <= 2097152 (2^21) for a prefill, row strides >= d_inner
+ *      and multiples of 8 elements, every pointer 16-byte aligned (int32 index vectors: 4-byte), and
+ *      norm_eps >= 0.
  *  - Errors: every entry point returns JM_OK (0) or a negative jm_status.  Arguments are validated on
  *    the host before anything is enqueued; on an error nothing is launched and no output is written.
  *    NaN / Inf in the inputs propagate and are not reported.  No C++ exception crosses this ABI.
@@ -171,6 +172,39 @@ int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights
                                const void* x, const void* z, void* out,
                                void* conv_state_pool, float* ssm_state_pool, int32_t pool_size,
                                const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace jm_mixer_prefill_varlen needs for these dims (0 if the dims are invalid). */
+size_t jm_mixer_prefill_varlen_workspace_size(const jm_mixer_dims* dims);
+
+/*
+ * Prefill of a packed batch of variable-length sequences, the prefill side of serving with continuous
+ * batching (Jamba Guide, aifetchly blog, "Production Engineering: Serving & Hardware Best Practices"):
+ * prompts of different lengths run in one call with no padding.  Each sequence gets exactly the result of
+ * jm_mixer_prefill on its own tokens and states (up to rounding); no state crosses from one sequence to
+ * the next.
+ *   dims->batch       number of sequences;  dims->seqlen  total tokens of all of them (the packed length)
+ *   x, z              in   [seqlen, row_stride]: the sequences' tokens one after another
+ *   out               out  [seqlen, C]
+ *   cu_seqlens        DEVICE int32 [batch + 1], 4-byte aligned: sequence s is packed tokens
+ *                     [cu_seqlens[s], cu_seqlens[s+1]); cu_seqlens[0] = 0, non-decreasing,
+ *                     cu_seqlens[batch] = seqlen.  Empty sequences are allowed (their states carry over).
+ *                     The host does not read these values; offsets that break the rules give unspecified
+ *                     results, but every access stays inside the buffers described here.
+ *   states            slots == NULL: conv_state_* [batch, C, K-1] and ssm_state_* [batch, C, N] float32,
+ *                     sequence s at row s.  slots != NULL (DEVICE int32 [batch], 4-byte aligned): pools of
+ *                     pool_size rows, sequence s at row slots[s]; the valid entries must be distinct, and an
+ *                     entry outside [0, pool_size) runs from zero states and stores none.
+ *                     conv_state_in / ssm_state_in may be NULL (zeros); the outputs are required and may
+ *                     alias the inputs (in-place update of a state pool).  Rows no sequence names are
+ *                     left untouched.
+ *   workspace         scratch of at least jm_mixer_prefill_varlen_workspace_size(dims) bytes.
+ */
+int jm_mixer_prefill_varlen(const jm_mixer_dims* dims, const jm_mixer_weights* weights,
+                            const void* x, const void* z, void* out, const int32_t* cu_seqlens,
+                            const void* conv_state_in, void* conv_state_out,
+                            const float* ssm_state_in, float* ssm_state_out,
+                            const int32_t* slots, int32_t pool_size,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* jm_status_string(int status);

@@ -10,4 +10,4 @@ from ._lib import (JM_BF16, JM_F32, JMError, Mixer, Dims, Weights, WorkspaceLayo
                    call_prefill, decode_workspace_size, lib, make_dims, pack_weights, prefill_workspace_size,
                    status_string, workspace_layout)
 from ._lib import Layer, LayerDims, LayerWeights, call_layer, layer_workspace_size, make_layer_dims  # noqa: F401
-from ._lib import call_decode_step_slots  # noqa: F401
+from ._lib import call_decode_step_slots, call_prefill_varlen, varlen_workspace_size  # noqa: F401

@@ -98,6 +98,16 @@ def lib() -> ctypes.CDLL:
         L.jm_layer_decode_step_slots.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, ctypes.c_int32, V, V,
                                                  S, V]
         L.jm_layer_decode_step_slots.restype = I
+        L.jm_mixer_prefill_varlen.argtypes = [P(Dims), P(Weights), V, V, V, V, V, V, V, V, V, ctypes.c_int32, V, S,
+                                              V]
+        L.jm_mixer_prefill_varlen.restype = I
+        L.jm_layer_prefill_varlen.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, V, V, V, V,
+                                              ctypes.c_int32, V, S, V]
+        L.jm_layer_prefill_varlen.restype = I
+        L.jm_mixer_prefill_varlen_workspace_size.argtypes = [P(Dims)]
+        L.jm_mixer_prefill_varlen_workspace_size.restype = S
+        L.jm_layer_prefill_varlen_workspace_size.argtypes = [P(LayerDims)]
+        L.jm_layer_prefill_varlen_workspace_size.restype = S
         for name in ("jm_layer_prefill_workspace_size", "jm_layer_decode_workspace_size"):
             f = getattr(L, name)
             f.argtypes = [P(LayerDims)]
@@ -161,6 +171,24 @@ def call_decode_step_slots(dims: Dims, weights: Weights, x, z, out, conv_pool, s
     """The raw state-pool decode entry point on integer device pointers (None for NULL)."""
     return lib().jm_mixer_decode_step_slots(_ref(dims), _ref(weights), x, z, out, conv_pool, ssm_pool, pool_size,
                                             slots, ws, ws_bytes, stream)
+
+
+def call_prefill_varlen(dims: Dims, weights: Weights, x, z, out, cu_seqlens, conv_in, conv_out, h_in, h_out,
+                       slots, pool_size: int, ws, ws_bytes: int, stream: int) -> int:
+    """The raw packed-batch prefill entry point on integer device pointers (None for NULL)."""
+    return lib().jm_mixer_prefill_varlen(_ref(dims), _ref(weights), x, z, out, cu_seqlens, conv_in, conv_out, h_in,
+                                         h_out, slots, pool_size, ws, ws_bytes, stream)
+
+
+def varlen_workspace_size(dims: Dims) -> int:
+    return int(lib().jm_mixer_prefill_varlen_workspace_size(ctypes.byref(dims)))
+
+
+def _check_cu(cu_seqlens: torch.Tensor) -> int:
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2 or \
+            not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector of n_seq + 1 offsets")
+    return int(cu_seqlens.shape[0]) - 1
 
 
 def _check_pools(conv_pool: torch.Tensor, ssm_pool: torch.Tensor, slots: torch.Tensor, batch: int) -> int:
@@ -276,6 +304,47 @@ class Mixer:
             raise JMError(s, "jm_mixer_decode_step")
         return out, conv_state_out, ssm_state_out
 
+    def prefill_varlen(self, x: torch.Tensor, z: torch.Tensor, cu_seqlens: torch.Tensor,
+                       conv_state: Optional[torch.Tensor] = None, ssm_state: Optional[torch.Tensor] = None,
+                       slots: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       conv_state_out: Optional[torch.Tensor] = None, ssm_state_out: Optional[torch.Tensor] = None,
+                       in_place: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """A packed batch: x, z [T, C] hold the sequences back to back, cu_seqlens (device int32 [n + 1])
+        delimits them.  States have one row per sequence, or are pools indexed by ``slots`` (device int32
+        [n]); with in_place=True the input states are updated in place."""
+        T, C = x.shape
+        nseq = _check_cu(cu_seqlens)
+        dims = self.dims(nseq, T, _row_stride(x, T), _row_stride(z, T))
+        nbytes = varlen_workspace_size(dims)
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_mixer_prefill_varlen_workspace_size")
+        ws = self.workspace(nbytes)
+        rows = nseq
+        pool = 0
+        if slots is not None:
+            if slots.dtype != torch.int32 or slots.shape != (nseq,) or not slots.is_contiguous():
+                raise ValueError(f"slots must be a contiguous int32 vector of length {nseq}")
+            ref = conv_state if conv_state is not None else conv_state_out
+            if ref is None:
+                raise ValueError("a state pool needs the conv state tensor (input or output) to size it")
+            rows = pool = int(ref.shape[0])
+        if out is None:
+            out = torch.empty((T, C), dtype=self.dtype, device=self.device)
+        if in_place:
+            conv_state_out, ssm_state_out = conv_state, ssm_state
+        if conv_state_out is None:
+            conv_state_out = torch.empty((rows, C, self.d_conv - 1), dtype=self.dtype, device=self.device)
+        if ssm_state_out is None:
+            ssm_state_out = torch.empty((rows, C, self.d_state), dtype=torch.float32, device=self.device)
+        _check_contiguous(out=out, conv_state=conv_state, conv_state_out=conv_state_out, ssm_state=ssm_state,
+                          ssm_state_out=ssm_state_out)
+        s = call_prefill_varlen(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(cu_seqlens), _ptr(conv_state),
+                                _ptr(conv_state_out), _ptr(ssm_state), _ptr(ssm_state_out), _ptr(slots), pool,
+                                _ptr(ws), ws.numel(), _stream(self.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_mixer_prefill_varlen")
+        return out, conv_state_out, ssm_state_out
+
     def decode_step_slots(self, x: torch.Tensor, z: torch.Tensor, conv_pool: torch.Tensor, ssm_pool: torch.Tensor,
                           slots: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """One token per sequence with the states in pools ([P, C, K-1] and [P, C, N]) updated in place at
@@ -376,6 +445,43 @@ class Layer:
         """x_res [B, d_model]; with in_place=True the states are updated in place."""
         co, so = (conv_state, ssm_state) if in_place else (None, None)
         return self._run(x_res, conv_state, ssm_state, out, co, so, True)
+
+    def prefill_varlen(self, x_res: torch.Tensor, cu_seqlens: torch.Tensor, conv_state: Optional[torch.Tensor] = None,
+                       ssm_state: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, in_place: bool = False
+                       ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """A packed batch x_res [T, d_model] split by cu_seqlens (device int32 [n + 1]); states per sequence or
+        in pools through ``slots``; with in_place=True the input states are updated in place."""
+        T = x_res.shape[0]
+        nseq = _check_cu(cu_seqlens)
+        m = self.mixer
+        C = m.d_inner
+        dims = self.dims(nseq, T)
+        nbytes = int(lib().jm_layer_prefill_varlen_workspace_size(ctypes.byref(dims)))
+        if nbytes == 0:
+            raise JMError(JM_ERR_INVALID_ARG, "jm_layer_prefill_varlen_workspace_size")
+        ws = self.workspace(nbytes)
+        rows, pool = nseq, 0
+        if slots is not None:
+            if slots.dtype != torch.int32 or slots.shape != (nseq,) or not slots.is_contiguous():
+                raise ValueError(f"slots must be a contiguous int32 vector of length {nseq}")
+            if conv_state is None:
+                raise ValueError("a state pool needs the conv state tensor to size it")
+            rows = pool = int(conv_state.shape[0])
+        if out is None:
+            out = torch.empty_like(x_res)
+        if in_place:
+            co, so = conv_state, ssm_state
+        else:
+            co = torch.empty((rows, C, m.d_conv - 1), dtype=self.dtype, device=self.device)
+            so = torch.empty((rows, C, m.d_state), dtype=torch.float32, device=self.device)
+        _check_contiguous(x_res=x_res, out=out, conv_state=conv_state, ssm_state=ssm_state, co=co, so=so)
+        s = lib().jm_layer_prefill_varlen(_ref(dims), _ref(self.packed), _ptr(x_res), _ptr(out), _ptr(cu_seqlens),
+                                          _ptr(conv_state), _ptr(co), _ptr(ssm_state), _ptr(so), _ptr(slots), pool,
+                                          _ptr(ws), ws.numel(), _stream(self.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_layer_prefill_varlen")
+        return out, co, so
 
     def decode_step_slots(self, x_res: torch.Tensor, conv_pool: torch.Tensor, ssm_pool: torch.Tensor,
                           slots: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -144,6 +144,114 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const T* __restrict__ x,
   }
 }
 
+// Packed batches: x is one axis of L tokens holding several sequences (v.cu).  A thread's run of tokens is
+// walked as segments that each lie in one sequence, the rows of a segment as in conv_silu_kernel; a
+// segment's left context comes from the sequence's earlier tokens or, at its start, from its conv state.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_silu_varlen_kernel(const T* __restrict__ x, int64_t xs,
+                                                               const T* __restrict__ conv_w,
+                                                               const T* __restrict__ conv_b,
+                                                               const T* __restrict__ conv_in, T* __restrict__ xc,
+                                                               int L, int C, int run, VarSeqs v) {
+  constexpr int V = Vec16<T>::n;
+  constexpr int S3 = kTaps - 1;
+  const int c0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
+  if (c0 >= C) return;
+  const int t0 = blockIdx.y * run;
+  const int t1 = min(L, t0 + run);
+
+  float w[V][kTaps], bias[V];
+  {
+    float wf[V * kTaps];
+#pragma unroll
+    for (int q = 0; q < V * kTaps; q += V) load16(conv_w + (int64_t)c0 * kTaps + q, wf + q);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < kTaps; ++j) w[i][j] = wf[i * kTaps + j];
+  }
+  if (conv_b) {
+    load16(conv_b + c0, bias);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) bias[i] = 0.0f;
+  }
+  const T* xb = x + c0;
+  T* ob = xc + c0;
+
+  // segments (offsets clamped so that every segment makes progress and every access stays in [0, L))
+  for (int u0 = t0; u0 < t1;) {
+    const int s = seq_of(v.cu, v.nseq, u0);
+    const int S = min(max(v.cu[s], 0), u0);
+    const int u1 = min(max(v.cu[s + 1], u0 + 1), t1);
+    // prev[j] = extended input at u0 - 3 + j: the sequence's own tokens, else entries of its conv state
+    // (3V contiguous elements for these V channels: three 16-byte loads)
+    float prev[S3][V];
+    if (u0 - S3 >= S) {
+#pragma unroll
+      for (int j = 0; j < S3; ++j) load16(xb + (int64_t)(u0 - S3 + j) * xs, prev[j]);
+    } else {
+      const int64_t srow = state_row(v.slots, v.pool, s);
+      float st[S3 * V];
+      if (conv_in && srow >= 0) {
+#pragma unroll
+        for (int q = 0; q < S3; ++q) load16(conv_in + (srow * C + c0) * S3 + q * V, st + q * V);
+      } else {
+#pragma unroll
+        for (int q = 0; q < S3 * V; ++q) st[q] = 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < S3; ++j) {
+        const int idx = u0 - S3 + j;
+        if (idx >= S) {
+          load16(xb + (int64_t)idx * xs, prev[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < V; ++i) prev[j][i] = st[i * S3 + (idx - S + S3)];
+        }
+      }
+    }
+    // the segment's rows in batches of kRows, the next batch in flight while one is computed
+    uint4 bufA[kRows], bufB[kRows];
+    auto load_rows = [&](int tb, uint4* buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < kRows; ++j)
+        buf[j] = *reinterpret_cast<const uint4*>(xb + (int64_t)min(tb + j, u1 - 1) * xs);
+    };
+    auto conv_rows = [&](int tb, const uint4* buf) __attribute__((always_inline)) {
+      const int count = min(kRows, u1 - tb);
+#pragma unroll
+      for (int j = 0; j < kRows; ++j) {
+        if (j >= count) break;
+        float cur[V], o[V];
+        unpack16<T>(buf[j], cur);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float u = bias[i];
+          u = fmaf(w[i][0], prev[0][i], u);
+          u = fmaf(w[i][1], prev[1][i], u);
+          u = fmaf(w[i][2], prev[2][i], u);
+          u = fmaf(w[i][3], cur[i], u);
+          o[i] = silu(u);
+          prev[0][i] = prev[1][i];
+          prev[1][i] = prev[2][i];
+          prev[2][i] = cur[i];
+        }
+        store16(ob + (int64_t)(tb + j) * C, o);
+      }
+    };
+    load_rows(u0, bufA);
+    for (int tb = u0; tb < u1; tb += 2 * kRows) {
+      if (tb + kRows < u1) load_rows(tb + kRows, bufB);
+      conv_rows(tb, bufA);
+      if (tb + kRows >= u1) break;
+      if (tb + 2 * kRows < u1) load_rows(tb + 2 * kRows, bufA);
+      conv_rows(tb + kRows, bufB);
+    }
+    u0 = u1;
+  }
+}
+
 // One token per sequence (decode): each thread takes 16 bytes of channels; a workgroup takes 256 such groups
 // of SPB consecutive sequences.  The conv weights (64 bytes per thread) are read once per workgroup, as
 // contiguous 16-byte lanes into LDS, and kept in registers for all its sequences.  A sequence's conv state
@@ -258,21 +366,79 @@ __global__ void state_passthrough_kernel(const T* __restrict__ conv_in, T* __res
   }
 }
 
+// Per sequence of a packed batch (grid.x) and channel (grid.y blocks of 256): the conv state out, i.e. the
+// last K-1 entries of the sequence's extended input (x after its conv state), and for an empty sequence
+// the SSM state carried over.  Each thread reads its entries before it writes them and no two threads
+// touch one element, so the outputs may alias the inputs.
+template <typename T>
+__global__ __launch_bounds__(256) void varlen_states_kernel(const T* x, int64_t xs, const T* conv_in, T* conv_out,
+                                                            const float* h0, float* h_out, int C, int L,
+                                                            VarSeqs v) {
+  constexpr int S3 = kTaps - 1;
+  const int s = blockIdx.x;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int64_t row = state_row(v.slots, v.pool, s);
+  if (row < 0) return;
+  const int S = min(max(v.cu[s], 0), L);
+  const int E = min(max(v.cu[s + 1], S), L);
+  const int len = E - S;
+  const int64_t base = (row * C + c) * S3;
+  T e[S3];
+#pragma unroll
+  for (int j = 0; j < S3; ++j) {
+    const int idx = len - S3 + j;   // position in the sequence; negative: an entry of the old state
+    if (idx >= 0) e[j] = x[(int64_t)(S + idx) * xs + c];
+    else e[j] = conv_in ? conv_in[base + idx + S3] : io<T>::from(0.0f);
+  }
+#pragma unroll
+  for (int j = 0; j < S3; ++j) conv_out[base + j] = e[j];
+  if (len == 0) {
+    const int64_t hb = (row * C + c) * 16;
+    float hv[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) hv[n] = h0 ? h0[hb + n] : 0.0f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) h_out[hb + n] = hv[n];
+  }
+}
+
 }  // namespace
 
+void launch_varlen_states(bool bf16, const void* x, int64_t xs, const void* conv_in, void* conv_out,
+                          const float* h0, float* h_out, int C, int L, const VarSeqs& v, hipStream_t st) {
+  dim3 grid((unsigned)v.nseq, (unsigned)((C + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(varlen_states_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, xs,
+                       (const bf16_t*)conv_in, (bf16_t*)conv_out, h0, h_out, C, L, v);
+  else
+    hipLaunchKernelGGL(varlen_states_kernel<float>, grid, dim3(256), 0, st, (const float*)x, xs,
+                       (const float*)conv_in, (float*)conv_out, h0, h_out, C, L, v);
+}
+
 void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
-                      const void* conv_in, void* xc, int B, int L, int C, hipStream_t st) {
+                      const void* conv_in, void* xc, int B, int L, int C, hipStream_t st, const VarSeqs& v) {
   const int V = bf16 ? 8 : 4;
   const int run = 32;
   dim3 block(256);
   dim3 grid((C / V + 255) / 256, (L + run - 1) / run, B);
-  if (bf16)
+  if (v.cu) {   // a packed batch: B == 1
+    if (bf16)
+      hipLaunchKernelGGL(conv_silu_varlen_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)x, xs,
+                         (const bf16_t*)conv_w, (const bf16_t*)conv_b, (const bf16_t*)conv_in, (bf16_t*)xc, L, C,
+                         run, v);
+    else
+      hipLaunchKernelGGL(conv_silu_varlen_kernel<float>, grid, block, 0, st, (const float*)x, xs,
+                         (const float*)conv_w, (const float*)conv_b, (const float*)conv_in, (float*)xc, L, C, run,
+                         v);
+  } else if (bf16) {
     hipLaunchKernelGGL(conv_silu_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)x, xs,
                        (const bf16_t*)conv_w, (const bf16_t*)conv_b, (const bf16_t*)conv_in, (bf16_t*)xc, L, C,
                        run);
-  else
+  } else {
     hipLaunchKernelGGL(conv_silu_kernel<float>, grid, block, 0, st, (const float*)x, xs, (const float*)conv_w,
                        (const float*)conv_b, (const float*)conv_in, (float*)xc, L, C, run);
+  }
 }
 
 void launch_conv_step(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,

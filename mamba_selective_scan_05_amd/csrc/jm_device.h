@@ -69,4 +69,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Packed variable-length batches: sequence s holds packed tokens [cu[s], cu[s+1]).  The sequence holding
+// token t is the last s in [0, nseq) with cu[s] <= t, which skips empty sequences; the search stays in
+// [0, nseq) whatever the offsets hold.  cu is read-only and wave-uniform here (scalar loads).
+__device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int t) {
+  int lo = 0, hi = nseq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The state row of sequence s: s itself without a pool, else its slot, -1 for a slot outside [0, pool).
+__device__ __forceinline__ int64_t state_row(const int32_t* slots, int pool, int s) {
+  if (!slots) return s;
+  const int r = slots[s];
+  return r >= 0 && r < pool ? r : -1;
+}
+
 }  // namespace jm

@@ -8,9 +8,27 @@
 
 namespace jm {
 
-// Causal depthwise conv1d (K = 4) + bias + SiLU over [B, L, C] -> xc [B*L, C] (contiguous).
+// A packed batch of variable-length sequences: sequence s holds packed tokens [cu[s], cu[s+1]) (device
+// int32 [nseq + 1]); its states are row s of the state tensors, or row slots[s] of pools of `pool` rows
+// (slots null: row s).  cu == nullptr: a plain [B, L] batch.
+struct VarSeqs {
+  const int32_t* cu;
+  const int32_t* slots;
+  int nseq;
+  int pool;
+};
+
+// Causal depthwise conv1d (K = 4) + bias + SiLU over [B, L, C] -> xc [B*L, C] (contiguous).  With v.cu the
+// input is one packed axis of L tokens (B = 1) and each sequence starts from its own conv state.
 void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
-                      const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
+                      const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st,
+                      const VarSeqs& v = VarSeqs{nullptr, nullptr, 0, 0});
+
+// Packed batches, per sequence: conv_state_out = the last K-1 entries of the sequence's extended input
+// (x after its conv state), and for an empty sequence ssm_state_out = ssm_state_in (zeros for null).
+// Every read of a row precedes its write, so outputs may alias inputs; run it after the conv.
+void launch_varlen_states(bool bf16, const void* x, int64_t x_stride, const void* conv_in, void* conv_out,
+                          const float* h0, float* h_out, int C, int L, const VarSeqs& v, hipStream_t st);
 
 // One token per sequence (seqlen 1): the same conv + SiLU -> xc [B, C], and the shifted conv state ->
 // conv_state_out [B, C, K-1] (may alias conv_state_in; zeros stand in for a NULL conv_state_in).  With
@@ -61,6 +79,13 @@ struct ScanArgs {
   // rows); a slot outside [0, pool) runs from a zero state and stores nothing.  Null: row b.
   const int32_t* slots;
   int pool;
+  // Packed variable-length batch (B = 1, L packed tokens): sequence s holds tokens [cu[s], cu[s+1]) and its
+  // SSM state is state row s (or slots[s]); the conv state is written by launch_varlen_states.  snap
+  // [P, N, C]: the initial state of the last sequence starting strictly inside a piece and running past it,
+  // saved by the local pass for the full pass (which must not read h0 rows other pieces may overwrite).
+  const int32_t* cu;
+  int nseq;
+  float* snap;
 };
 
 // The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.
@@ -70,15 +95,16 @@ void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* mark
 // The mixer behind jm_mixer_prefill / jm_mixer_decode_step, for the layer entry points: the workspace bytes
 // of a call (a negative jm_status for invalid dims), every check of a call without launching anything, and
 // the validated call itself (each a jm_status).
-int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode);
-// With slots (decode only), the states are pools of `pool` rows indexed by slots[b], as in
-// jm_mixer_decode_step_slots.
+// With slots, the states are pools of `pool` rows indexed by slots[b], as in jm_mixer_decode_step_slots;
+// with cu (prefill only), a packed batch as in jm_mixer_prefill_varlen.
+int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode, bool varlen = false);
 int mixer_validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
                    const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-                   bool decode, const int32_t* slots = nullptr, int pool = 0);
+                   bool decode, const int32_t* slots = nullptr, int pool = 0, const int32_t* cu = nullptr);
 int mixer_run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
               const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-              void* stream, bool decode, const int32_t* slots = nullptr, int pool = 0);
+              void* stream, bool decode, const int32_t* slots = nullptr, int pool = 0,
+              const int32_t* cu = nullptr);
 
 // seqlen == 0: copy the states through (zeros for a NULL input).
 void launch_state_passthrough(bool bf16, const void* conv_in, void* conv_out, const float* h0, float* h_out,

@@ -155,16 +155,17 @@ struct LayerPlan {
   int64_t off_hn, off_xz, off_y, off_mixer, off_gemm, total;
 };
 
-int layer_plan(const jm_layer_dims* d, bool decode, LayerPlan* p) {
+// varlen: a packed batch (d->mixer.batch sequences, d->mixer.seqlen tokens in all)
+int layer_plan(const jm_layer_dims* d, bool decode, LayerPlan* p, bool varlen = false) {
   if (!d) return JM_ERR_INVALID_ARG;
   if (d->d_model < 1 || !(d->layer_norm_eps >= 0.0f)) return JM_ERR_INVALID_ARG;
   if (d->d_model % 8 != 0) return JM_ERR_UNSUPPORTED;
   p->md = d->mixer;
   p->md.x_row_stride = 2 * (int64_t)d->mixer.d_inner;
   p->md.z_row_stride = 2 * (int64_t)d->mixer.d_inner;
-  const int64_t mws = jm::mixer_workspace_bytes(&p->md, decode);
+  const int64_t mws = jm::mixer_workspace_bytes(&p->md, decode, varlen);
   if (mws < 0) return (int)mws;   // the mixer's own validation code
-  p->T = (int64_t)d->mixer.batch * (decode ? 1 : d->mixer.seqlen);
+  p->T = varlen ? d->mixer.seqlen : (int64_t)d->mixer.batch * (decode ? 1 : d->mixer.seqlen);
   p->C = d->mixer.d_inner;
   p->Dm = d->d_model;
   p->esize = d->mixer.io_dtype == JM_BF16 ? 2 : 4;
@@ -180,9 +181,10 @@ int layer_plan(const jm_layer_dims* d, bool decode, LayerPlan* p) {
 
 int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void* x_res, void* out,
               const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-              void* stream, bool decode, const int32_t* slots = nullptr, int pool = 0) {
+              void* stream, bool decode, const int32_t* slots = nullptr, int pool = 0,
+              const int32_t* cu = nullptr) {
   LayerPlan p;
-  int s = layer_plan(dims, decode, &p);
+  int s = layer_plan(dims, decode, &p, cu != nullptr);
   if (s != JM_OK) return s;
   if (!lw || !lw->norm_w || !lw->in_proj_w || !lw->out_proj_w) return JM_ERR_INVALID_ARG;
   const void* ptrs[] = {lw->norm_w, lw->in_proj_w, lw->out_proj_w, x_res, out, ws};
@@ -203,11 +205,11 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
   // everything the mixer checks, before the norm and in_proj are enqueued
   if ((s = jm::mixer_validate(&p.md, &lw->mixer, p.T > 0 ? xz : nullptr, p.T > 0 ? xz + p.C * p.esize : nullptr,
                               p.T > 0 ? y : nullptr, conv_in, conv_out, h0, h_out, mws, mws_bytes, decode, slots,
-                              pool)) != JM_OK)
+                              pool, cu)) != JM_OK)
     return s;
   if (p.T == 0) {   // no tokens: the mixer copies the states through
     return jm::mixer_run(&p.md, &lw->mixer, nullptr, nullptr, nullptr, conv_in, conv_out, h0, h_out, mws,
-                         mws_bytes, stream, decode);
+                         mws_bytes, stream, decode, slots, pool, cu);
   }
   (void)hipGetLastError();
   if (bf16)
@@ -222,7 +224,7 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
       JM_OK)
     return s;
   if ((s = jm::mixer_run(&p.md, &lw->mixer, xz, xz + p.C * p.esize, y, conv_in, conv_out, h0, h_out, mws,
-                         mws_bytes, stream, decode, slots, pool)) != JM_OK)
+                         mws_bytes, stream, decode, slots, pool, cu)) != JM_OK)
     return s;
   return gemm(bf16, y, p.C, lw->out_proj_w, p.C, out, p.Dm, x_res, p.Dm, p.T, p.Dm, p.C, gws, st);
 }
@@ -261,6 +263,20 @@ int jm_layer_decode_step_slots(const jm_layer_dims* dims, const jm_layer_weights
   if (!slots) return JM_ERR_INVALID_ARG;
   return layer_run(dims, weights, x_res, out, conv_state_pool, conv_state_pool, ssm_state_pool, ssm_state_pool,
                    workspace, workspace_bytes, stream, true, slots, pool_size);
+}
+
+size_t jm_layer_prefill_varlen_workspace_size(const jm_layer_dims* dims) {
+  LayerPlan p;
+  return layer_plan(dims, false, &p, true) == JM_OK ? (size_t)p.total : 0;
+}
+
+int jm_layer_prefill_varlen(const jm_layer_dims* dims, const jm_layer_weights* weights, const void* x_res,
+                            void* out, const int32_t* cu_seqlens, const void* conv_state_in, void* conv_state_out,
+                            const float* ssm_state_in, float* ssm_state_out, const int32_t* slots,
+                            int32_t pool_size, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return JM_ERR_INVALID_ARG;
+  return layer_run(dims, weights, x_res, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out,
+                   workspace, workspace_bytes, stream, false, slots, pool_size, cu_seqlens);
 }
 
 }  // extern "C"

@@ -12,6 +12,7 @@ constexpr int kN = 16;       // d_state the kernels are built for
 constexpr int kTaps = 4;     // d_conv the kernels are built for
 constexpr int kMaxR = 512;   // dt_rank bound of the norm kernel
 constexpr int64_t kAlign = 256;
+constexpr int kMaxSeqlen = 1 << 21;   // tokens of a prefill call (the conv's grid rows stay under 65536)
 
 // Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.
 #ifndef JM_SCAN_WAVE_TARGET
@@ -31,7 +32,17 @@ struct Plan {
   bool narrow;   // x_proj in 32-column groups (few tokens)
   int P, Lp;     // scan pieces per sequence, tokens per piece
   int64_t xs, zs;
-  int64_t off_xc, off_dbc, off_dln, off_bc, off_delta, off_loc, off_cin, total;
+  int nseq;      // packed batches: number of sequences (the plan itself runs B = 1 over L = all tokens)
+  int64_t off_xc, off_dbc, off_dln, off_bc, off_delta, off_loc, off_cin, off_snap, total;
+};
+
+// Optional parts of a call: per-stage events, a state pool (slots), a packed batch (cu_seqlens).
+struct Extras {
+  void** events = nullptr;
+  int n_events = 0;
+  const int32_t* slots = nullptr;
+  int pool = 0;
+  const int32_t* cu = nullptr;
 };
 
 int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -40,6 +51,7 @@ int check_dims(const jm_mixer_dims* d, bool decode) {
   if (!d) return JM_ERR_INVALID_ARG;
   if (d->batch < 1 || d->d_inner < 1 || d->dt_rank < 1) return JM_ERR_INVALID_ARG;
   if (!decode && d->seqlen < 0) return JM_ERR_INVALID_ARG;
+  if (!decode && d->seqlen > kMaxSeqlen) return JM_ERR_UNSUPPORTED;
   if (!(d->norm_eps >= 0.0f)) return JM_ERR_INVALID_ARG;
   if (d->io_dtype != JM_F32 && d->io_dtype != JM_BF16) return JM_ERR_UNSUPPORTED;
   if (d->d_state != kN || d->d_conv != kTaps) return JM_ERR_UNSUPPORTED;
@@ -52,9 +64,11 @@ int check_dims(const jm_mixer_dims* d, bool decode) {
   return JM_OK;
 }
 
-Plan make_plan(const jm_mixer_dims* d, bool decode) {
+// varlen: a packed batch of d->batch sequences holding d->seqlen tokens in all, planned as one sequence
+Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
   Plan p;
-  p.B = d->batch;
+  p.nseq = d->batch;
+  p.B = varlen ? 1 : d->batch;
   p.L = decode ? 1 : d->seqlen;
   p.C = d->d_inner;
   p.N = d->d_state;
@@ -104,11 +118,13 @@ Plan make_plan(const jm_mixer_dims* d, bool decode) {
   p.off_dln = off;   off += align_up(p.T * p.R * p.esize);
   p.off_bc = off;    off += align_up(p.T * 2 * p.N * 4);
   p.off_delta = off; off += align_up(p.T * p.C * p.esize);
+  p.off_loc = p.off_cin = p.off_snap = -1;
   if (p.P > 1) {
     p.off_loc = off; off += align_up((int64_t)p.B * p.P * (p.N + 1) * p.C * 4);
     p.off_cin = off; off += align_up((int64_t)p.B * p.P * p.N * p.C * 4);
-  } else {
-    p.off_loc = p.off_cin = -1;
+    if (varlen) {
+      p.off_snap = off; off += align_up((int64_t)p.P * p.N * p.C * 4);
+    }
   }
   p.total = off > 0 ? off : kAlign;
   return p;
@@ -143,17 +159,18 @@ struct StageMarks {
 // Every check of a call, before anything is enqueued.
 int validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
              const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-             bool decode, const int32_t* slots = nullptr, int pool = 0) {
+             bool decode, const int32_t* slots = nullptr, int pool = 0, const int32_t* cu = nullptr) {
   int s = check_dims(dims, decode);
   if (s != JM_OK) return s;
   if ((s = check_weights(w)) != JM_OK) return s;
-  const Plan p = make_plan(dims, decode);
+  const Plan p = make_plan(dims, decode, cu != nullptr);
   if (!conv_out || !h_out) return JM_ERR_INVALID_ARG;
   if (decode && (!conv_in || !h0)) return JM_ERR_INVALID_ARG;
-  if (slots) {   // a state pool: decode only, at least one row, int32 indices
-    if (!decode || pool < 1) return JM_ERR_INVALID_ARG;
+  if (slots) {   // a state pool: decode or packed prefill, at least one row, int32 indices
+    if ((!decode && !cu) || pool < 1) return JM_ERR_INVALID_ARG;
     if (((uintptr_t)slots & 3u) != 0) return JM_ERR_ALIGNMENT;
   }
+  if (cu && ((uintptr_t)cu & 3u) != 0) return JM_ERR_ALIGNMENT;
   if (p.L > 0 && (!x || !z || !out)) return JM_ERR_INVALID_ARG;
   const void* ptrs[] = {x, z, out, conv_in, conv_out, h0, h_out, ws};
   for (const void* q : ptrs)
@@ -164,11 +181,16 @@ int validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x
 
 int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
         const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-        void* stream, bool decode, void** events = nullptr, int n_events = 0, const int32_t* slots = nullptr,
-        int pool = 0) {
-  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool);
+        void* stream, bool decode, const Extras& ex = Extras()) {
+  void** events = ex.events;
+  const int n_events = ex.n_events;
+  const int32_t* slots = ex.slots;
+  const int pool = ex.pool;
+  const bool varlen = ex.cu != nullptr;
+  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool, ex.cu);
   if (s != JM_OK) return s;
-  const Plan p = make_plan(dims, decode);
+  const Plan p = make_plan(dims, decode, varlen);
+  const jm::VarSeqs vs{ex.cu, slots, p.nseq, pool};
   if (events) {
     if (n_events < JM_STAGES + 1) return JM_ERR_INVALID_ARG;
     for (int i = 0; i <= JM_STAGES; ++i)
@@ -180,7 +202,10 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   (void)hipGetLastError();  // clear a stale error so the check below reports this call's launches only
   if (p.L == 0) {
     marks.mark(0);
-    jm::launch_state_passthrough(p.bf16, conv_in, conv_out, h0, h_out, p.B, p.C, st);
+    if (varlen)   // every sequence is empty: its states carry over
+      jm::launch_varlen_states(p.bf16, x, p.xs, conv_in, conv_out, h0, h_out, p.C, 0, vs, st);
+    else
+      jm::launch_state_passthrough(p.bf16, conv_in, conv_out, h0, h_out, p.B, p.C, st);
     for (int i = 1; i <= JM_STAGES; ++i) marks.mark(i);
     return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
   }
@@ -193,12 +218,15 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
 
   marks.mark(0);
   // one token per sequence: the single-step conv also writes the conv state, so the scan skips it
-  const bool step = p.L == 1;
-  if (step)
+  const bool step = p.L == 1 && !varlen;
+  if (step) {
     jm::launch_conv_step(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, conv_out, p.B, p.C, st, slots,
                          pool);
-  else
-    jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st);
+  } else {
+    jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st, vs);
+    // a packed batch's conv states (and the states of its empty sequences), once the conv has read them
+    if (varlen) jm::launch_varlen_states(p.bf16, x, p.xs, conv_in, conv_out, h0, h_out, p.C, p.L, vs, st);
+  }
   marks.mark(1);
   jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st);
   marks.mark(2);
@@ -220,7 +248,7 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.x = x;
   a.x_stride = p.xs;
   a.conv_in = conv_in;
-  a.conv_out = step ? nullptr : conv_out;
+  a.conv_out = step || varlen ? nullptr : conv_out;
   a.loc = p.P > 1 ? (float*)(base + p.off_loc) : nullptr;
   a.cin = p.P > 1 ? (float*)(base + p.off_cin) : nullptr;
   a.B = p.B;
@@ -230,6 +258,9 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.Lp = p.Lp;
   a.slots = slots;
   a.pool = pool;
+  a.cu = ex.cu;
+  a.nseq = p.nseq;
+  a.snap = p.off_snap >= 0 ? (float*)(base + p.off_snap) : nullptr;
   // the scan records events[4] (local pass), events[5] (carry pass) and events[6] (full pass)
   jm::launch_scan(p.bf16, a, st, events ? &marks.ev[4] : nullptr);
   marks.mark(JM_STAGES);
@@ -240,23 +271,26 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
 
 namespace jm {
 
-int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode) {
+int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode, bool varlen) {
   const int s = check_dims(dims, decode);
   if (s != JM_OK) return s;
-  return make_plan(dims, decode).total;
+  return make_plan(dims, decode, varlen).total;
 }
 
 int mixer_validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
                    const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-                   bool decode, const int32_t* slots, int pool) {
-  return validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool);
+                   bool decode, const int32_t* slots, int pool, const int32_t* cu) {
+  return validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool, cu);
 }
 
 int mixer_run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
               const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-              void* stream, bool decode, const int32_t* slots, int pool) {
-  return run(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, stream, decode, nullptr, 0, slots,
-             pool);
+              void* stream, bool decode, const int32_t* slots, int pool, const int32_t* cu) {
+  Extras ex;
+  ex.slots = slots;
+  ex.pool = pool;
+  ex.cu = cu;
+  return run(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, stream, decode, ex);
 }
 
 }  // namespace jm
@@ -292,8 +326,30 @@ int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights
                                int32_t pool_size, const int32_t* slots, void* workspace, size_t workspace_bytes,
                                void* stream) {
   if (!slots) return JM_ERR_INVALID_ARG;
+  Extras ex;
+  ex.slots = slots;
+  ex.pool = pool_size;
   return run(dims, weights, x, z, out, conv_state_pool, conv_state_pool, ssm_state_pool, ssm_state_pool,
-             workspace, workspace_bytes, stream, true, nullptr, 0, slots, pool_size);
+             workspace, workspace_bytes, stream, true, ex);
+}
+
+size_t jm_mixer_prefill_varlen_workspace_size(const jm_mixer_dims* dims) {
+  if (check_dims(dims, false) != JM_OK) return 0;
+  return (size_t)make_plan(dims, false, true).total;
+}
+
+int jm_mixer_prefill_varlen(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
+                            const void* z, void* out, const int32_t* cu_seqlens, const void* conv_state_in,
+                            void* conv_state_out, const float* ssm_state_in, float* ssm_state_out,
+                            const int32_t* slots, int32_t pool_size, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!cu_seqlens) return JM_ERR_INVALID_ARG;
+  Extras ex;
+  ex.cu = cu_seqlens;
+  ex.slots = slots;
+  ex.pool = pool_size;
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
+             workspace_bytes, stream, false, ex);
 }
 
 int jm_mixer_prefill_profiled(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
@@ -301,8 +357,11 @@ int jm_mixer_prefill_profiled(const jm_mixer_dims* dims, const jm_mixer_weights*
                               const float* ssm_state_in, float* ssm_state_out, void* workspace,
                               size_t workspace_bytes, void* stream, void** events, int n_events) {
   if (!events) return JM_ERR_INVALID_ARG;
+  Extras ex;
+  ex.events = events;
+  ex.n_events = n_events;
   return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
-             workspace_bytes, stream, false, events, n_events);
+             workspace_bytes, stream, false, ex);
 }
 
 int jm_mixer_decode_step_profiled(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
@@ -310,8 +369,11 @@ int jm_mixer_decode_step_profiled(const jm_mixer_dims* dims, const jm_mixer_weig
                                   const float* ssm_state_in, float* ssm_state_out, void* workspace,
                                   size_t workspace_bytes, void* stream, void** events, int n_events) {
   if (!events) return JM_ERR_INVALID_ARG;
+  Extras ex;
+  ex.events = events;
+  ex.n_events = n_events;
   return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
-             workspace_bytes, stream, true, events, n_events);
+             workspace_bytes, stream, true, ex);
 }
 
 const char* jm_stage_name(int stage) { return stage >= 0 && stage < JM_STAGES ? kStageNames[stage] : "?"; }

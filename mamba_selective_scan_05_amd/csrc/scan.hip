@@ -80,6 +80,7 @@ __device__ __forceinline__ void load_a2(const T* A_log, int c, float* a2) {
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 __device__ __forceinline__ int hslot(int l, int q) { return l * 16 + ((q ^ ((l >> 2) & 3)) << 2); }
 __device__ __forceinline__ void state_load(const float* src, float* hs, int lane, float* h) {
+  __builtin_amdgcn_wave_barrier();                    // the tile may still be in use by an earlier store
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int g = q * 64 + lane;                      // 16-byte chunk g of the wave's 4 KB
@@ -107,7 +108,11 @@ __device__ __forceinline__ void state_store(float* dst, float* hs, int lane, con
 }
 
 // FULL = false: the local pass (end state + delta sum of a piece); FULL = true: the output pass.
-template <typename T, bool FULL>
+// VAR: one packed axis of several sequences (a.cu).  A piece is walked as segments that each lie in one
+// sequence; at a sequence start the state is reset to that sequence's initial state, and the local pass
+// marks the piece as reset (its end state then no longer depends on the incoming state).  The full pass
+// stores a sequence's final state where it ends.
+template <typename T, bool FULL, bool VAR>
 __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   const int c = blockIdx.x * 64 + threadIdx.x;
   const int p = blockIdx.y;
@@ -118,18 +123,32 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float hs[64 * kN];
   float a2[kN], h[kN];
   load_a2((const T*)a.A_log, c, a2);
-  // the SSM state row of sequence b: b itself, or its slot in a state pool (-1: none)
+  // the SSM state row of sequence b (VAR: of the sequence holding the piece's first token): b itself, or
+  // its slot in a state pool (-1: none)
+  int s = 0;
   int64_t srow = b;
-  if (a.slots) {
-    const int s = a.slots[b];
-    srow = s >= 0 && s < a.pool ? s : -1;
+  if (VAR) {
+    s = seq_of(a.cu, a.nseq, t0);
+    srow = state_row(a.slots, a.pool, s);
+  } else if (a.slots) {
+    srow = state_row(a.slots, a.pool, b);
   }
+  auto init_state = [&](int64_t row) __attribute__((always_inline)) {
+    if (a.h0 && row >= 0) {
+      state_load(a.h0 + (row * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+    } else {
+#pragma unroll
+      for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+    }
+  };
+  bool reset = false;
   if (FULL && P > 1) {
     const float* src = a.cin + ((int64_t)b * P + p) * kN * C + c;
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = src[(int64_t)n * C];
-  } else if (p == 0 && a.h0 && srow >= 0) {
-    state_load(a.h0 + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+  } else if (VAR ? a.cu[s] == t0 : p == 0) {
+    init_state(srow);
+    reset = true;
   } else {
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
@@ -157,7 +176,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   // never has to be merged into a half register before it is needed.  Prefetch indices are clamped to the
   // piece, so loads past its end re-read its last token instead of branching.
   typedef typename Raw<T>::type R;
-  auto load_batch = [&](int i0, R* d, R* x, R* z) {
+  auto load_batch = [&](int i0, R* d, R* x, R* z) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const uint32_t i = (uint32_t)min(i0 + j, n_tok - 1);
@@ -170,7 +189,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   // The decay factors exp(delta_t * A) of a token are computed as one group: the multiplies, then all the
   // exponentials back to back.  Issued one by one between the dependent FMAs, each exponential costs the
   // vector ALU noticeably more (measured: the full pass 7% and the local pass 9% slower).
-  auto decay = [&](R d, float* e) {
+  auto decay = [&](R d, float* e) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < kN; ++n) e[n] = Raw<T>::f(d) * a2[n];
     __builtin_amdgcn_sched_barrier(0);
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
   // SiLU(z) of a batch of tokens, each transcendental kind as one group
-  auto gates = [&](const R* z, float* g) {
+  auto gates = [&](const R* z, float* g) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) g[j] = Raw<T>::f(z[j]) * -kLog2e;
     __builtin_amdgcn_sched_barrier(0);
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
   // one token given its decay factors e and gate g: B_t / C_t come in as wave-uniform values
-  auto step = [&](int i, R draw, R xraw, const float* e, float g, const float* Bt, const float* Ct) {
+  auto step = [&](int i, R draw, R xraw, const float* e, float g, const float* Bt, const float* Ct) __attribute__((always_inline)) {
     const float dt = Raw<T>::f(draw);
     const float xv = Raw<T>::f(xraw);
     const float u = dt * xv;
@@ -214,7 +233,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   // so the only wait for them is "all scalar loads done": each token first waits for its own B / C, then
   // requests the next token's, then computes, and the request stays in flight for a whole token.
   float Bc[kN], Cc[kN];
-  auto load_bc = [&](int i, float* Bt, float* Ct) {
+  auto load_bc = [&](int i, float* Bt, float* Ct) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < kN; ++n) {
       Bt[n] = bcp[(int64_t)i * (2 * kN) + n];
@@ -223,7 +242,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   };
   // A full batch of kBatch tokens starting at i0 whose inputs are in d/x/z; on entry Bc/Cc hold token i0's
   // B/C, on exit token i0 + kBatch's (clamped to the piece).
-  auto run_full = [&](int i0, const R* d, const R* x, const R* z) {
+  auto run_full = [&](int i0, const R* d, const R* x, const R* z) __attribute__((always_inline)) {
     float g[kBatch];
     if (FULL) gates(z, g);
 #pragma unroll
@@ -250,42 +269,80 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   // no-prefetch path, i.e. wait for the loads just issued.  Fewer than kBatch leftover tokens run one at a
   // time afterwards.
   R dA[kBatch], xA[kBatch], zA[kBatch], dB[kBatch], xB[kBatch], zB[kBatch];
-  const int nfull = n_tok / kBatch;
-  if (n_tok > 0) {
-    load_batch(0, dA, xA, zA);
-    load_bc(0, Bc, Cc);
-  }
-  int k = 0;
-  for (; k + 2 <= nfull; k += 2) {
-    load_batch((k + 1) * kBatch, dB, xB, zB);
-    run_full(k * kBatch, dA, xA, zA);
-    load_batch((k + 2) * kBatch, dA, xA, zA);
-    run_full((k + 1) * kBatch, dB, xB, zB);
-  }
-  if (k < nfull) {   // an odd last full batch, already loaded into dA / xA / zA
-    run_full(k * kBatch, dA, xA, zA);
-    ++k;
-  }
-  for (int i = k * kBatch; i < n_tok; ++i) {
-    const R d = Raw<T>::ld(dres, voff, (uint32_t)i * row_bytes);
-    const R x = Raw<T>::ld(xres, voff, (uint32_t)i * row_bytes);
-    float e[kN];
+  // tokens [i0, i1) of the piece
+  auto run_range = [&](int i0, int i1) __attribute__((always_inline)) {
+    const int nfull = (i1 - i0) / kBatch;
+    if (i1 > i0) {
+      load_batch(i0, dA, xA, zA);
+      load_bc(i0, Bc, Cc);
+    }
+    int k = 0;
+    for (; k + 2 <= nfull; k += 2) {
+      load_batch(i0 + (k + 1) * kBatch, dB, xB, zB);
+      run_full(i0 + k * kBatch, dA, xA, zA);
+      load_batch(i0 + (k + 2) * kBatch, dA, xA, zA);
+      run_full(i0 + (k + 1) * kBatch, dB, xB, zB);
+    }
+    if (k < nfull) {   // an odd last full batch, already loaded into dA / xA / zA
+      run_full(i0 + k * kBatch, dA, xA, zA);
+      ++k;
+    }
+    for (int i = i0 + k * kBatch; i < i1; ++i) {
+      const R d = Raw<T>::ld(dres, voff, (uint32_t)i * row_bytes);
+      const R x = Raw<T>::ld(xres, voff, (uint32_t)i * row_bytes);
+      float e[kN];
 #pragma unroll
-    for (int n = 0; n < kN; ++n) e[n] = exp2_fast(Raw<T>::f(d) * a2[n]);
-    const float g = FULL ? silu(Raw<T>::f(Raw<T>::ld(zres, voff, (uint32_t)i * zrow_bytes))) : 0.0f;
-    float Bt[kN], Ct[kN];
-    load_bc(i, Bt, Ct);
-    step(i, d, x, e, g, Bt, Ct);
+      for (int n = 0; n < kN; ++n) e[n] = exp2_fast(Raw<T>::f(d) * a2[n]);
+      const float g = FULL ? silu(Raw<T>::f(Raw<T>::ld(zres, voff, (uint32_t)i * zrow_bytes))) : 0.0f;
+      float Bt[kN], Ct[kN];
+      load_bc(i, Bt, Ct);
+      step(i, d, x, e, g, Bt, Ct);
+    }
+  };
+
+  if (!VAR) {
+    run_range(0, n_tok);
+  } else {
+    // Segments, each inside one sequence (offsets clamped so every segment makes progress).  A sequence
+    // that starts inside the piece and runs past it has its initial state read by the local pass (before
+    // any final state is written) and saved in snap for the full pass: the piece that writes its final
+    // state may run concurrently with this one, and the state rows may be updated in place.
+    float* snap = a.snap + (int64_t)p * kN * C + c;
+    for (int u = 0; u < n_tok;) {
+      const int end = a.cu[s + 1] - t0;            // the sequence's end, relative to the piece
+      const int u1 = min(max(end, u + 1), n_tok);
+      run_range(u, u1);
+      if (FULL && end <= n_tok && srow >= 0)      // the sequence ends in this piece
+        state_store(a.h_out + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+      u = u1;
+      if (u >= n_tok) break;
+      s = seq_of(a.cu, a.nseq, t0 + u);            // the next non-empty sequence starts at u
+      srow = state_row(a.slots, a.pool, s);
+      const bool spans = a.cu[s + 1] - t0 > n_tok;
+      if (FULL && spans) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = snap[(int64_t)n * C];
+      } else {
+        init_state(srow);
+        if (!FULL && spans) {
+#pragma unroll
+          for (int n = 0; n < kN; ++n) snap[(int64_t)n * C] = h[n];
+        }
+      }
+      reset = true;
+    }
   }
 
   if (!FULL) {
+    // the delta sum, or -1 when the piece resets the state (its end state is then independent of its
+    // incoming state)
     float* dst = a.loc + ((int64_t)b * P + p) * (kN + 1) * C + c;
 #pragma unroll
     for (int n = 0; n < kN; ++n) dst[(int64_t)n * C] = h[n];
-    dst[(int64_t)kN * C] = sdt;
+    dst[(int64_t)kN * C] = VAR && reset ? -1.0f : sdt;
     return;
   }
-  if (p == P - 1) {
+  if (!VAR && p == P - 1) {
     if (srow < 0) return;
     state_store(a.h_out + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
     // conv state (unless the conv step wrote it): the last K-1 entries of the extended input (old state
@@ -306,10 +363,12 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   }
 }
 
-template <typename T>
+// VAR: a piece whose first token starts a sequence takes that sequence's initial state as its incoming
+// state, and a piece marked as reset (delta sum -1) passes on its local end state alone.
+template <typename T, bool VAR>
 __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict__ loc, const T* __restrict__ A_log,
                                                          const float* __restrict__ h0, float* __restrict__ cin,
-                                                         int B, int C, int P) {
+                                                         int B, int C, int P, ScanArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over (b, n, c)
   if (i >= (int64_t)B * kN * C) return;
   const int c = (int)(i % C);
@@ -318,31 +377,47 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
   const float a2 = -exp2_fast(io<T>::ld(A_log + (int64_t)c * kN + n) * kLog2e) * kLog2e;
   const float* lb = loc + (int64_t)b * P * (kN + 1) * C;
   float* cb = cin + (int64_t)b * P * kN * C;
-  cb[(int64_t)n * C + c] = h0 ? h0[((int64_t)b * C + c) * kN + n] : 0.0f;
-  float H = lb[(int64_t)n * C + c];   // piece 0 started from h0: its end state is exact
+  float H = 0.0f;
+  if (!VAR) {
+    const int64_t row = state_row(a.slots, a.pool, b);
+    cb[(int64_t)n * C + c] = h0 && row >= 0 ? h0[(row * C + c) * kN + n] : 0.0f;
+    H = lb[(int64_t)n * C + c];   // piece 0 started from h0: its end state is exact
+  }
   // pieces in groups of 8: all loads of a group are issued before its serial combine
   constexpr int kG = 8;
-  for (int p0 = 1; p0 < P; p0 += kG) {
-    float hl[kG], sd[kG];
+  for (int p0 = VAR ? 0 : 1; p0 < P; p0 += kG) {
+    float hl[kG], sd[kG], hi[kG];
+    bool starts[kG];
 #pragma unroll
     for (int j = 0; j < kG; ++j) {
       const int p = min(p0 + j, P - 1);
       const float* lp = lb + (int64_t)p * (kN + 1) * C;
       hl[j] = lp[(int64_t)n * C + c];
       sd[j] = lp[(int64_t)kN * C + c];
+      starts[j] = false;
+      hi[j] = 0.0f;
+      if (VAR) {
+        const int tp = p * a.Lp;
+        const int s = seq_of(a.cu, a.nseq, tp);
+        starts[j] = a.cu[s] == tp;
+        const int64_t row = state_row(a.slots, a.pool, s);
+        if (starts[j] && h0 && row >= 0) hi[j] = h0[(row * C + c) * kN + n];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kG; ++j) {
       const int p = p0 + j;
       if (p < P) {
+        if (VAR && starts[j]) H = hi[j];
         cb[((int64_t)p * kN + n) * C + c] = H;
-        H = fmaf(exp2_fast(sd[j] * a2), H, hl[j]);   // unused after the last piece
+        // unused after the last piece
+        H = VAR && sd[j] < 0.0f ? hl[j] : fmaf(exp2_fast(sd[j] * a2), H, hl[j]);
       }
     }
   }
 }
 
-template <typename T>
+template <typename T, bool VAR>
 void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   auto mark = [&](int i) {
     if (marks) (void)hipEventRecord((hipEvent_t)marks[i], st);
@@ -350,24 +425,29 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   mark(0);
   if (a.P > 1) {
     dim3 gl(a.C / 64, a.P - 1, a.B);
-    hipLaunchKernelGGL((scan_pass_kernel<T, false>), gl, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((scan_pass_kernel<T, false, VAR>), gl, dim3(64), 0, st, a);
   }
   mark(1);
   if (a.P > 1) {
     const int64_t n = (int64_t)a.B * kN * a.C;
-    hipLaunchKernelGGL(scan_carry_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.loc,
-                       (const T*)a.A_log, a.h0, a.cin, a.B, a.C, a.P);
+    hipLaunchKernelGGL((scan_carry_kernel<T, VAR>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.loc,
+                       (const T*)a.A_log, a.h0, a.cin, a.B, a.C, a.P, a);
   }
   mark(2);
   dim3 gf(a.C / 64, a.P, a.B);
-  hipLaunchKernelGGL((scan_pass_kernel<T, true>), gf, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((scan_pass_kernel<T, true, VAR>), gf, dim3(64), 0, st, a);
 }
 
 }  // namespace
 
 void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks) {
-  if (bf16) run_scan<bf16_t>(a, st, marks);
-  else run_scan<float>(a, st, marks);
+  if (a.cu) {
+    if (bf16) run_scan<bf16_t, true>(a, st, marks);
+    else run_scan<float, true>(a, st, marks);
+  } else {
+    if (bf16) run_scan<bf16_t, false>(a, st, marks);
+    else run_scan<float, false>(a, st, marks);
+  }
 }
 
 }  // namespace jm

@@ -165,3 +165,36 @@ def test_state_pool_decode_validation_before_launch():
     assert lcall(0, FAKE) == _lib.JM_ERR_INVALID_ARG
     assert lcall(4, FAKE + 2) == _lib.JM_ERR_ALIGNMENT
     assert lcall(4, FAKE, ws_bytes=16) == _lib.JM_ERR_WORKSPACE
+
+
+def test_varlen_prefill_validation_before_launch():
+    d = _dims(batch=3, seqlen=64)
+    w = _weights()
+    call = lambda cu=FAKE, slots=None, pool=0, ws_bytes=WS_BIG, dims=d: jm.call_prefill_varlen(
+        dims, w, FAKE, FAKE, FAKE, cu, FAKE, FAKE, FAKE, FAKE, slots, pool, FAKE, ws_bytes, 0)
+    assert call(cu=None) == _lib.JM_ERR_INVALID_ARG             # no offsets
+    assert call(cu=FAKE + 2) == _lib.JM_ERR_ALIGNMENT           # int32 offsets need 4-byte alignment
+    assert call(slots=FAKE, pool=0) == _lib.JM_ERR_INVALID_ARG  # a pool needs rows
+    assert call(slots=FAKE + 1, pool=4) == _lib.JM_ERR_ALIGNMENT
+    assert call(ws_bytes=16) == _lib.JM_ERR_WORKSPACE           # everything else was accepted
+    assert call(slots=FAKE, pool=4, ws_bytes=16) == _lib.JM_ERR_WORKSPACE
+    too_long = _dims(batch=3, seqlen=(1 << 21) + 1)
+    assert jm.varlen_workspace_size(too_long) == 0
+    assert call(dims=too_long) == _lib.JM_ERR_UNSUPPORTED
+    # the workspace of a packed batch depends on the total length, not on how it is split
+    n1 = jm.varlen_workspace_size(jm.make_dims(1, 4096, 8192, 256, jm.JM_BF16))
+    n8 = jm.varlen_workspace_size(jm.make_dims(8, 4096, 8192, 256, jm.JM_BF16))
+    assert n1 > 0 and n8 == n1
+    # zero tokens: x, z, out may be NULL
+    assert jm.call_prefill_varlen(_dims(batch=2, seqlen=0), w, None, None, None, FAKE, None, FAKE, None, FAKE,
+                                  None, 0, FAKE, 0, 0) == _lib.JM_ERR_WORKSPACE
+    mixer_w = jm.Weights(*([FAKE] * 10))
+    lw = jm.LayerWeights(FAKE, FAKE, FAKE, mixer_w)
+    ld = jm.make_layer_dims(3, 64, 128, 16, jm.JM_BF16, 64)
+    L = _lib.lib()
+    assert L.jm_layer_prefill_varlen_workspace_size(ctypes.byref(ld)) > 0
+    lcall = lambda cu=FAKE, ws_bytes=WS_BIG: L.jm_layer_prefill_varlen(
+        ctypes.byref(ld), ctypes.byref(lw), FAKE, FAKE, cu, None, FAKE, None, FAKE, None, 0, FAKE, ws_bytes, None)
+    assert lcall(cu=None) == _lib.JM_ERR_INVALID_ARG
+    assert lcall(cu=FAKE + 2) == _lib.JM_ERR_ALIGNMENT
+    assert lcall(ws_bytes=16) == _lib.JM_ERR_WORKSPACE

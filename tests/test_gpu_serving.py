@@ -1,5 +1,6 @@
-"""GPU parity of the serving-style entry points: decode over pools of per-sequence states
-(jm_mixer_decode_step_slots, jm_layer_decode_step_slots), through the C ABI.
+"""GPU parity of the serving-style entry points, through the C ABI: decode over pools of per-sequence states
+(jm_mixer_decode_step_slots, jm_layer_decode_step_slots) and prefill of packed variable-length batches
+(jm_mixer_prefill_varlen, jm_layer_prefill_varlen) against the fp64 oracle.
 
 A serving engine batches whichever sequences are generating and keeps their conv / SSM states in pools;
 the step reads and writes row slots[b] in place.  Checked here, over several steps with the pool carried
@@ -17,8 +18,8 @@ import pytest
 import torch
 
 import oracle
-from jm_inputs import MixerConfig, make_decode_tokens, make_layer_input, make_layer_weights, make_state, \
-    make_weights, to_f64
+from jm_inputs import MixerConfig, make_activations, make_decode_tokens, make_layer_input, make_layer_weights, \
+    make_state, make_weights, to_f64
 from parity_util import assert_bitwise, assert_close, log, weights_f64
 
 pytestmark = pytest.mark.gpu
@@ -158,3 +159,120 @@ def test_layer_decode_slots():
     assert_close("conv pool", conv_pool, c64, "bf16")
     for r in (1, 3, 5):
         assert torch.equal(conv_pool[r], conv0[r]) and torch.equal(ssm_pool[r], ssm0[r]), r
+
+
+# ----------------------------------------------------------------------------- packed variable-length prefill
+
+# lengths chosen against the scan's 128-token pieces at d_inner 256 (checked below): sequences that span
+# pieces, one that starts exactly at a piece start, sequences starting inside a piece and running past it,
+# empty sequences, sequences shorter than the conv window, and a last sequence inside the last piece
+VARLEN_LENS = [200, 0, 56, 1, 2, 300, 129, 70, 0]
+
+
+def _packed(cfg, lens, seed_cfg):
+    T = sum(lens)
+    a = make_activations(seed_cfg.replace(batch=1, seqlen=T), DEV)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    return a["x"][0].contiguous(), a["z"][0].contiguous(), cu
+
+
+def _check_varlen(io, with_state, slots=None, pool=None, seed=44, lens=VARLEN_LENS, C=256, R=16, in_place=False):
+    import mamba_selective_scan_05_amd as jm
+    nseq = len(lens)
+    rows = nseq if slots is None else pool
+    cfg = MixerConfig(f"varlen_{io}", batch=rows, seqlen=1, d_inner=C, dt_rank=R, io_dtype=io, seed=seed,
+                      with_state=True)
+    w = make_weights(cfg, DEV)
+    x, z, cu = _packed(cfg, lens, cfg)
+    T = x.shape[0]
+    st = make_state(cfg, DEV) if with_state else {"conv_state": None, "ssm_state": None}
+    m = jm.Mixer(w, R, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    lay = jm.workspace_layout(jm.make_dims(1, T, C, R, jm.JM_BF16 if io == "bf16" else jm.JM_F32))
+    log(f"[varlen_{io}] lens={lens} T={T} C={C} pieces={lay.scan_chunks} state={with_state} slots={slots} "
+        f"in_place={in_place}")
+    sl = None if slots is None else torch.tensor(slots, dtype=torch.int32, device=DEV)
+    # outputs start as copies of the inputs (or NaN), so rows the call must not touch are checkable
+    if with_state:
+        cs_in, hs_in = st["conv_state"].clone(), st["ssm_state"].clone()
+        co, so = (cs_in, hs_in) if in_place else (cs_in.clone(), hs_in.clone())
+    else:
+        cs_in = hs_in = None
+        co = torch.full((rows, C, 3), float("nan"), dtype=cfg.torch_dtype, device=DEV)
+        so = torch.full((rows, C, 16), float("nan"), device=DEV)
+    before_c, before_h = co.clone(), so.clone()
+    out, co, so = m.prefill_varlen(x, z, cu, cs_in, hs_in, slots=sl, conv_state_out=co, ssm_state_out=so)
+    torch.cuda.synchronize()
+    c64 = None if not with_state else to_f64(st["conv_state"])
+    h64 = None if not with_state else to_f64(st["ssm_state"])
+    ro, rc, rh = oracle.mixer_prefill_varlen(to_f64(x), to_f64(z), cu.cpu().numpy(), weights_f64(w), R,
+                                             cfg.d_state, cfg.norm_eps, c64, h64, slots)
+    assert_close("out", out, ro, io)
+    named = sorted({r for r in (range(nseq) if slots is None else slots) if 0 <= r < rows})
+    for r in named:
+        assert_close(f"ssm_state[{r}]", so[r], rh[r], io)
+        assert_bitwise(f"conv_state[{r}]", co[r], torch.from_numpy(rc[r]).to(cfg.torch_dtype))
+    for r in set(range(rows)) - set(named):
+        assert torch.equal(co[r].view(torch.uint8), before_c[r].view(torch.uint8)), r
+        assert torch.equal(so[r].view(torch.uint8), before_h[r].view(torch.uint8)), r
+    return lay
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("with_state", [True, False])
+def test_prefill_varlen_small(io, with_state):
+    lay = _check_varlen(io, with_state)
+    assert lay.scan_chunks == 6     # 758 tokens in pieces of 128: the boundaries above fall as intended
+
+
+def test_prefill_varlen_pool_in_place():
+    # sequences read and write pool rows in place; a padding entry (-1) and an out-of-range entry (9) run
+    # from zero states and store nothing; the pool rows no sequence names stay untouched
+    slots = [6, 2, -1, 0, 4, 9, 1, 7, 3]
+    _check_varlen("bf16", True, slots=slots, pool=9, seed=45, in_place=True)
+
+
+def test_prefill_varlen_single_piece_and_all_empty():
+    import mamba_selective_scan_05_amd as jm
+    _check_varlen("bf16", True, lens=[5, 0, 40, 3], seed=46)         # one scan piece, no carries
+    # no tokens at all: every sequence is empty and keeps its states
+    cfg = MixerConfig("varlen_empty", batch=3, seqlen=1, d_inner=128, dt_rank=16, io_dtype="bf16", seed=47,
+                      with_state=True)
+    w = make_weights(cfg, DEV)
+    st = make_state(cfg, DEV)
+    m = jm.Mixer(w, 16)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    out, co, so = m.prefill_varlen(x, x, cu, st["conv_state"], st["ssm_state"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+    assert torch.equal(co, st["conv_state"]) and torch.equal(so, st["ssm_state"])
+
+
+def test_prefill_varlen_jamba_widths_4k_tokens():
+    # Jamba v0.1's widths (d_inner 8192, dt_rank 256) with 4096 packed tokens of mixed lengths, the
+    # token count of the 4K prefill workload
+    _check_varlen("bf16", True, lens=[1000, 37, 2048, 0, 500, 511], C=8192, R=256, seed=48)
+
+
+def test_layer_prefill_varlen():
+    import mamba_selective_scan_05_amd as jm
+    lens = [150, 0, 3, 300, 60]
+    C, R, Dm = 128, 16, 64
+    nseq, T = len(lens), sum(lens)
+    cfg = MixerConfig("layer_varlen", batch=nseq, seqlen=1, d_inner=C, dt_rank=R, io_dtype="bf16", seed=49,
+                      with_state=True, d_model=Dm)
+    w = make_weights(cfg, DEV)
+    lw = make_layer_weights(cfg, DEV)
+    st = make_state(cfg, DEV)
+    xr = make_layer_input(cfg.replace(batch=1, seqlen=T), DEV)[0].contiguous()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    layer = jm.Layer(lw, w, R, cfg.d_state, cfg.d_conv, cfg.norm_eps, 1e-6)
+    log(f"[layer_varlen] lens={lens} C={C} d_model={Dm}")
+    out, co, so = layer.prefill_varlen(xr, cu, st["conv_state"], st["ssm_state"])
+    torch.cuda.synchronize()
+    ro, rc, rh = oracle.layer_prefill_varlen(to_f64(xr), cu.cpu().numpy(), weights_f64(lw), weights_f64(w), R,
+                                             cfg.d_state, cfg.norm_eps, 1e-6, to_f64(st["conv_state"]),
+                                             to_f64(st["ssm_state"]))
+    assert_close("out", out, ro, "bf16")
+    assert_close("ssm_state", so, rh, "bf16")
+    assert_close("conv_state", co, rc, "bf16")
