@@ -8,7 +8,8 @@ seeded synthetic tensors already resident in HBM.  W untimed warmup steps, then 
 device synchronisations; value = tokens / second.  A second timed pass records HIP events between the
 library's kernels (jm_mixer_prefill_profiled) for the per-kernel roofline.  The decode workload (B=256,
 one token per sequence, the fp32 state rotated over 4 sets so that it streams from HBM) is timed the same
-way and reported alongside.  The fp64 CPU oracle is timed on the host on the same prefill workload as a
+way and reported alongside, as are the whole Mamba layer around the mixer and the serving-style calls
+(a packed batch of prompts of mixed lengths, decode over a state pool).  The fp64 CPU oracle is timed on the host on the same prefill workload as a
 baseline.
 
 Prints one JSON line.  Only one GPU is supported: --gpus N with N > 1 exits with a message.
@@ -346,6 +347,95 @@ def time_layer(jm, cfg, steps, warmup, decode):
             "tokens_per_s": round(B * L / (ms * 1e-3), 1), "gemm_flops_per_step": gemm_flops}
 
 
+def time_serving(jm, steps, warmup):
+    """The serving-style calls at Jamba v0.1's widths: a packed batch of 8 prompts of mixed lengths (4096
+    tokens) prefilled in place into rows of a 64-row state pool, and a B=256 decode step over a 1024-row pool
+    (four disjoint slot sets rotated, so the states stream from HBM as in the plain decode timing)."""
+    import torch
+    from jm_inputs import SERVING_CONFIGS, SERVING_POOL_ROWS, make_activations, make_state, make_weights, \
+        packed_lengths, pool_slots
+
+    dev = "cuda"
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+
+    def timed(step):
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # packed variable-length prefill
+    cfg, rows = SERVING_CONFIGS[0], SERVING_POOL_ROWS[0]
+    w = make_weights(cfg, dev)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    T, C = cfg.seqlen, cfg.d_inner
+    a = make_activations(cfg.replace(batch=1), dev)
+    x, z = a["x"][0].contiguous(), a["z"][0].contiguous()
+    lens = packed_lengths(T, cfg.batch, cfg.seed)
+    cu = torch.tensor([0] + [sum(lens[:k + 1]) for k in range(len(lens))], dtype=torch.int32, device=dev)
+    slots = torch.tensor(pool_slots(cfg.batch, rows, cfg.seed), dtype=torch.int32, device=dev)
+    st = make_state(cfg.replace(batch=rows), dev)
+    cp, hp = st["conv_state"], st["ssm_state"]
+    out = torch.empty((T, C), dtype=cfg.torch_dtype, device=dev)
+    dims = m.dims(cfg.batch, T)
+    ws = m.workspace(jm.varlen_workspace_size(dims))
+
+    def pre_step(i):
+        s = jm.call_prefill_varlen(dims, m.packed, x.data_ptr(), z.data_ptr(), out.data_ptr(), cu.data_ptr(),
+                                   cp.data_ptr(), cp.data_ptr(), hp.data_ptr(), hp.data_ptr(), slots.data_ptr(),
+                                   rows, ws.data_ptr(), ws.numel(), stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_mixer_prefill_varlen")
+
+    log(f"serving {cfg.name}: lengths {lens}")
+    ms = timed(pre_step)
+    res["varlen_prefill"] = {"workload": f"{cfg.name}: {cfg.batch} prompts of mixed lengths packed into {T} "
+                                         f"tokens, states in place in a {rows}-row pool",
+                             "lengths": lens, "us_per_step": round(ms * 1e3, 2),
+                             "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    del m, w, x, z, a, st, cp, hp, out
+    # decode over a state pool
+    cfg, rows = SERVING_CONFIGS[1], SERVING_POOL_ROWS[1]
+    w = make_weights(cfg, dev)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    B, C = cfg.batch, cfg.d_inner
+    st = make_state(cfg.replace(batch=rows), dev)
+    cp, hp = st["conv_state"], st["ssm_state"]
+    perm = pool_slots(rows, rows, cfg.seed)
+    sets = [torch.tensor(perm[k * B:(k + 1) * B], dtype=torch.int32, device=dev) for k in range(rows // B)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    xs = torch.randn((8, B, C), generator=g, device=dev).to(cfg.torch_dtype)
+    zs = torch.randn((8, B, C), generator=g, device=dev).to(cfg.torch_dtype)
+    out = torch.empty((B, C), dtype=cfg.torch_dtype, device=dev)
+    dims = m.dims(B, 1)
+    ws = m.workspace(jm.decode_workspace_size(dims))
+
+    def dec_step(i):
+        s = jm.call_decode_step_slots(dims, m.packed, xs[i % 8].data_ptr(), zs[i % 8].data_ptr(), out.data_ptr(),
+                                      cp.data_ptr(), hp.data_ptr(), rows, sets[i % len(sets)].data_ptr(),
+                                      ws.data_ptr(), ws.numel(), stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_mixer_decode_step_slots")
+
+    log(f"serving {cfg.name}")
+    ms = timed(dec_step)
+    db = decode_bytes(B, C, cfg.d_state, cfg.dt_rank, cfg.d_conv, 2)
+    gbs = db / (ms * 1e-3) / 1e9
+    res["decode_slots"] = {"workload": f"{cfg.name}: B={B} decode, states in a {rows}-row pool, "
+                                       f"{len(sets)} disjoint slot sets rotated",
+                           "batch": B, "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(B / (ms * 1e-3), 1),
+                           "alg_bytes": db, "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def run_decode(jm, dcfg, args, hip):
     log(f"decode {dcfg.name}: warmup {args.warmup}, steps {args.steps}")
     dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
@@ -372,6 +462,8 @@ def main():
     ap.add_argument("--config", type=int, default=1, choices=(1, 2, 3),
                     help="prefill workload: 1 = B1 L4096 (default), 2 = B8 L4096, 3 = B1 L262144")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the serving-style timings (packed prefill, pooled-state decode)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workload and print its figures (for per-workload profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -477,6 +569,14 @@ def main():
                     lay[name]["gemm_tflops_estimate"] = round(tflops, 1)
             log(f"  {name}: {lay[name]['us_per_step']:.1f} us per step")
         result["layer"] = lay
+    if not args.no_serving and args.config == 1:
+        result["serving"] = time_serving(jm, args.steps, args.warmup)
+        # the packed batch holds the same 4096 tokens as the B=1 prefill timed above
+        result["serving"]["varlen_prefill"]["vs_B1_L4096_prefill"] = round(
+            result["serving"]["varlen_prefill"]["tokens_per_s"] / value, 3)
+        if "decode" in result:
+            result["serving"]["decode_slots"]["vs_plain_decode"] = round(
+                result["decode"]["us_per_step"] / result["serving"]["decode_slots"]["us_per_step"], 3)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {min(args.cpu_tokens, cfg.seqlen)} tokens ...")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)

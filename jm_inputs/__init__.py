@@ -24,6 +24,11 @@ the residual width (4096 in Jamba v0.1):
     in_proj_w       ~ N(0, 1/d_model)         [2 d_inner, d_model], rows ordered x | z
     out_proj_w      ~ N(0, 1/d_inner)         [d_model, d_inner]
 
+Serving workloads (continuous batching) add:
+    packed lengths  nseq - 1 distinct cut points drawn uniformly from 1 .. T-1 (numpy default_rng(seed)),
+                    so the prompts of one packed batch vary widely in length
+    pool slots      distinct pool rows drawn uniformly without replacement (numpy default_rng(seed))
+
 Every tensor draws from its own torch generator whose seed is a child of numpy's SeedSequence(1000 + cfg),
 spawned in a fixed order, so a tensor's values do not depend on which other tensors were generated.
 """
@@ -32,7 +37,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 import torch
@@ -85,6 +90,29 @@ CONFIGS = (
     MixerConfig("jamba_decode_B256_x128", batch=256, seqlen=1, d_inner=8192, decode_steps=128,
                 with_state=True, seed=1004),
 )
+
+
+# Serving-style workloads at Jamba v0.1's widths: 4096 tokens of 8 prompts of mixed lengths prefilled as one
+# packed batch into rows of a 64-row state pool; decode of 256 sequences whose states sit in a 1024-row pool.
+SERVING_CONFIGS = (
+    CONFIGS[1].replace(name="jamba_varlen_prefill_T4096_n8_pool64", batch=8, with_state=True, seed=1201),
+    CONFIGS[4].replace(name="jamba_decode_slots_B256_pool1024", seed=1202),
+)
+SERVING_POOL_ROWS = (64, 1024)
+
+
+def packed_lengths(total: int, nseq: int, seed: int) -> List[int]:
+    """Lengths of nseq prompts packed into ``total`` tokens (each >= 1): nseq - 1 distinct cut points drawn
+    uniformly from 1 .. total - 1."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, total), nseq - 1, replace=False))
+    return [int(v) for v in np.diff(np.concatenate([[0], cuts, [total]]))]
+
+
+def pool_slots(n: int, pool: int, seed: int) -> List[int]:
+    """n distinct rows of a pool of ``pool`` rows, drawn uniformly without replacement."""
+    rng = np.random.default_rng(seed)
+    return [int(v) for v in rng.choice(pool, n, replace=False)]
 
 
 def _child_seeds(seed: int) -> Dict[str, int]:
