@@ -29,6 +29,9 @@ Serving workloads (continuous batching) add:
                     so the prompts of one packed batch vary widely in length
     pool slots      distinct pool rows drawn uniformly without replacement (numpy default_rng(seed))
 
+The gated scan on its own (the training forward and backward) takes delta ~ U(1e-3, 0.2) directly,
+B and C ~ N(0, 1) as the RMSNorms leave them, dout ~ N(0, 1), h0 and dh_final ~ N(0, 0.1).
+
 Every tensor draws from its own torch generator whose seed is a child of numpy's SeedSequence(1000 + cfg),
 spawned in a fixed order, so a tensor's values do not depend on which other tensors were generated.
 """
@@ -47,6 +50,7 @@ _TENSOR_ORDER = (
     "x", "z", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D",
     "dt_norm_w", "b_norm_w", "c_norm_w", "conv_state", "ssm_state", "x_steps", "z_steps",
     "layer_norm_w", "in_proj_w", "out_proj_w", "x_res", "x_res_steps",
+    "scan_delta", "scan_bc", "scan_dout", "scan_dh_final",
 )
 
 
@@ -228,6 +232,28 @@ def make_layer_input(cfg: MixerConfig, device: str = "cpu", steps: int = 0) -> t
     if steps:
         return _normal((cfg.batch, steps, cfg.d_model), 1.0, s["x_res_steps"], device).to(cfg.torch_dtype)
     return _normal((cfg.batch, cfg.seqlen, cfg.d_model), 1.0, s["x_res"], device).to(cfg.torch_dtype)
+
+
+def make_scan_problem(cfg: MixerConfig, device: str = "cpu", with_state: bool = True) -> Dict[str, torch.Tensor]:
+    """Inputs of the gated scan alone and of its backward (training): x = xc, z ~ N(0, 1) and delta ~
+    U(1e-3, 0.2) [B, L, C] in the I/O dtype; bc ~ N(0, 1) [B*L, 2N] fp32 (B then C, as the RMSNorms leave
+    them); A_log and D as the mixer's; dout ~ N(0, 1) [B, L, C]; h0 and dh_final ~ N(0, 0.1) fp32."""
+    s = _child_seeds(cfg.seed)
+    B, L, C, N = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state
+    w = make_weights(cfg, device)
+    a = make_activations(cfg, device)
+    p = {
+        "x": a["x"].contiguous(), "z": a["z"].contiguous(),
+        "delta": _uniform((B, L, C), 1e-3, 0.2, s["scan_delta"], device).to(cfg.torch_dtype),
+        "bc": _normal((B * L, 2 * N), 1.0, s["scan_bc"], device),
+        "A_log": w["A_log"], "D": w["D"],
+        "dout": _normal((B, L, C), 1.0, s["scan_dout"], device).to(cfg.torch_dtype),
+        "h0": None, "dh_final": None,
+    }
+    if with_state:
+        p["h0"] = make_state(cfg, device)["ssm_state"]
+        p["dh_final"] = _normal((B, C, N), math.sqrt(0.1), s["scan_dh_final"], device)
+    return p
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

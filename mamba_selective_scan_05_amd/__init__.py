@@ -11,3 +11,4 @@ from ._lib import (JM_BF16, JM_F32, JMError, Mixer, Dims, Weights, WorkspaceLayo
                    status_string, workspace_layout)
 from ._lib import Layer, LayerDims, LayerWeights, call_layer, layer_workspace_size, make_layer_dims  # noqa: F401
 from ._lib import call_decode_step_slots, call_prefill_varlen, varlen_workspace_size  # noqa: F401
+from ._lib import ScanDims, scan_backward, scan_dims, scan_forward, scan_workspace_size  # noqa: F401

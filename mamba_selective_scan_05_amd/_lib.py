@@ -1,4 +1,4 @@
-"""ctypes binding of libjm_mixer.so (the C ABI in include/jm_mixer.h and include/jm_layer.h).
+"""ctypes binding of libjm_mixer.so (the C ABI in include/jm_mixer.h, include/jm_layer.h and include/jm_scan.h).
 
 The functions here only marshal arguments: torch tensors provide device memory and the stream, their
 data pointers go to the library, and every step of the mixer runs in the library's HIP kernels.  If the
@@ -56,6 +56,11 @@ class LayerDims(ctypes.Structure):
 LAYER_WEIGHT_NAMES = ("norm_w", "in_proj_w", "out_proj_w")
 
 
+class ScanDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("d_inner", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("io_dtype", ctypes.c_int32)]
+
+
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES] + [("mixer", Weights)]
 
@@ -108,6 +113,14 @@ def lib() -> ctypes.CDLL:
         L.jm_mixer_prefill_varlen_workspace_size.restype = S
         L.jm_layer_prefill_varlen_workspace_size.argtypes = [P(LayerDims)]
         L.jm_layer_prefill_varlen_workspace_size.restype = S
+        L.jm_scan_forward.argtypes = [P(ScanDims)] + [V] * 10 + [S, V]
+        L.jm_scan_forward.restype = I
+        L.jm_scan_backward.argtypes = [P(ScanDims)] + [V] * 17 + [S, V]
+        L.jm_scan_backward.restype = I
+        for name in ("jm_scan_forward_workspace_size", "jm_scan_backward_workspace_size"):
+            f = getattr(L, name)
+            f.argtypes = [P(ScanDims)]
+            f.restype = S
         for name in ("jm_layer_prefill_workspace_size", "jm_layer_decode_workspace_size"):
             f = getattr(L, name)
             f.argtypes = [P(LayerDims)]
@@ -502,3 +515,63 @@ class Layer:
         if s != JM_OK:
             raise JMError(s, "jm_layer_decode_step_slots")
         return out
+
+
+# ----------------------------------------------------------------------------- the gated scan alone (training)
+
+def scan_dims(batch: int, seqlen: int, d_inner: int, io_dtype: int, d_state: int = 16) -> ScanDims:
+    return ScanDims(batch, seqlen, d_inner, d_state, io_dtype)
+
+
+def scan_workspace_size(dims: ScanDims, backward: bool = False) -> int:
+    f = lib().jm_scan_backward_workspace_size if backward else lib().jm_scan_forward_workspace_size
+    return int(f(ctypes.byref(dims)))
+
+
+def _scan_ws(dims: ScanDims, backward: bool, device) -> torch.Tensor:
+    n = scan_workspace_size(dims, backward)
+    if n == 0:
+        raise JMError(JM_ERR_INVALID_ARG, "jm_scan_*_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def scan_forward(x: torch.Tensor, delta: torch.Tensor, z: torch.Tensor, bc: torch.Tensor, A_log: torch.Tensor,
+                 D: torch.Tensor, h0: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The gated scan forward (jm_scan_forward): x, delta, z [B, L, C] in the I/O dtype, bc [B*L, 2N] fp32,
+    A_log [C, N], D [C]; returns (out [B, L, C], h_out [B, C, N] fp32)."""
+    B, L, C = x.shape
+    _check_contiguous(x=x, delta=delta, z=z, bc=bc, A_log=A_log, D=D, h0=h0)
+    dims = scan_dims(B, L, C, _io_dtype(x), A_log.shape[1])
+    ws = _scan_ws(dims, False, x.device)
+    out = torch.empty_like(x)
+    h_out = torch.empty((B, C, A_log.shape[1]), dtype=torch.float32, device=x.device)
+    s = lib().jm_scan_forward(ctypes.byref(dims), _ptr(x), _ptr(delta), _ptr(z), _ptr(bc), _ptr(A_log), _ptr(D),
+                              _ptr(h0), _ptr(out), _ptr(h_out), _ptr(ws), ws.numel(), _stream(x.device))
+    if s != JM_OK:
+        raise JMError(s, "jm_scan_forward")
+    return out, h_out
+
+
+def scan_backward(x: torch.Tensor, delta: torch.Tensor, z: torch.Tensor, bc: torch.Tensor, A_log: torch.Tensor,
+                  D: torch.Tensor, dout: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                  dh_final: Optional[torch.Tensor] = None, need_dh0: bool = True) -> Dict[str, torch.Tensor]:
+    """Gradients of sum(dout * out) + sum(dh_final * h_L) (jm_scan_backward): returns dx, ddelta, dz (I/O
+    dtype), dbc [B*L, 2N], dA_log [C, N], dD [C] and dh0 [B, C, N] (fp32)."""
+    B, L, C = x.shape
+    N = A_log.shape[1]
+    _check_contiguous(x=x, delta=delta, z=z, bc=bc, A_log=A_log, D=D, dout=dout, h0=h0, dh_final=dh_final)
+    dims = scan_dims(B, L, C, _io_dtype(x), N)
+    ws = _scan_ws(dims, True, x.device)
+    dev = x.device
+    g = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dz": torch.empty_like(x),
+         "dbc": torch.empty((B * L, 2 * N), dtype=torch.float32, device=dev),
+         "dA_log": torch.empty((C, N), dtype=torch.float32, device=dev),
+         "dD": torch.empty((C,), dtype=torch.float32, device=dev),
+         "dh0": torch.empty((B, C, N), dtype=torch.float32, device=dev) if need_dh0 else None}
+    s = lib().jm_scan_backward(ctypes.byref(dims), _ptr(x), _ptr(delta), _ptr(z), _ptr(bc), _ptr(A_log), _ptr(D),
+                               _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dz"]),
+                               _ptr(g["dbc"]), _ptr(g["dA_log"]), _ptr(g["dD"]), _ptr(g["dh0"]), _ptr(ws), ws.numel(),
+                               _stream(dev))
+    if s != JM_OK:
+        raise JMError(s, "jm_scan_backward")
+    return g

@@ -91,6 +91,41 @@ struct ScanArgs {
 // The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.
 // marks (optional): events recorded before the local pass, the carry pass and the full pass.
 void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks = nullptr);
+// Only the local and carry passes (P > 1): every piece's incoming state -> a.cin.
+void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st);
+
+// Scan pieces for B sequences of L tokens over C channels: about a fixed number of waves in the full pass,
+// pieces of at least 128 tokens, each piece's rows (row_bytes apart) under 2 GiB.
+void scan_plan(int B, int L, int C, int64_t row_bytes, int* P, int* Lp);
+
+// Backward of the gated scan (training).  Pieces of kBwdPiece tokens; all [B*L, C] tensors contiguous.
+constexpr int kBwdPiece = 128;
+struct BwdArgs {
+  const void* xc;        // [B*L, C] io dtype
+  const void* delta;     // [B*L, C]
+  const void* z;         // [B*L, C]
+  const void* dout;      // [B*L, C]
+  const float* bc;       // [B*L, 2N]  B then C
+  const void* A_log;     // [C, N]
+  const void* D;         // [C]
+  const float* h0;       // [B, C, N] or null
+  const float* dh_final; // [B, C, N] or null
+  const float* cin;      // [B, P, N, C]  incoming states of the pieces (forward carry)
+  float* bloc;           // [B, P, N+1, C] backward local records
+  float* gin;            // [B, P, N, C]  incoming gradients of the pieces
+  float* pA;             // [B*P, C, N]
+  float* pD;             // [B*P, C]
+  float* pbc;            // [C/64, B*L, 2N]
+  void* dxc;             // [B*L, C] io dtype
+  void* ddelta;          // [B*L, C]
+  void* dz;              // [B*L, C]
+  float* dbc;            // [B*L, 2N]
+  float* dA_log;         // [C, N]
+  float* dD;             // [C]
+  float* dh0;            // [B, C, N] or null
+  int B, L, C, P;
+};
+void launch_scan_backward(bool bf16, const BwdArgs& a, hipStream_t st);
 
 // The mixer behind jm_mixer_prefill / jm_mixer_decode_step, for the layer entry points: the workspace bytes
 // of a call (a negative jm_status for invalid dims), every check of a call without launching anything, and

@@ -101,16 +101,8 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
   }
 
   // scan pieces
-  const int64_t waves = (int64_t)p.B * (p.C / 64);
-  int64_t want = (kScanWaveTarget + waves - 1) / waves;
-  int64_t lp = p.L > 0 ? (p.L + want - 1) / want : 1;
-  if (lp < kMinPiece) lp = kMinPiece;
-  // the scan addresses a piece through 32-bit byte offsets: keep each piece's rows under 2 GiB
   const int64_t row_bytes = (p.xs > p.zs ? (p.xs > p.C ? p.xs : p.C) : (p.zs > p.C ? p.zs : p.C)) * p.esize;
-  const int64_t max_rows = ((int64_t)1 << 31) / row_bytes - 1;
-  if (lp > max_rows) lp = max_rows;
-  p.Lp = (int)(lp < p.L ? lp : (p.L > 0 ? p.L : 1));
-  p.P = p.L > 0 ? (int)((p.L + p.Lp - 1) / p.Lp) : 1;
+  jm::scan_plan(p.B, p.L, p.C, row_bytes, &p.P, &p.Lp);
 
   int64_t off = 0;
   p.off_xc = off;    off += align_up(p.T * p.C * p.esize);
@@ -270,6 +262,18 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
 }  // namespace
 
 namespace jm {
+
+void scan_plan(int B, int L, int C, int64_t row_bytes, int* P, int* Lp) {
+  const int64_t waves = (int64_t)B * (C / 64);
+  const int64_t want = (kScanWaveTarget + waves - 1) / waves;
+  int64_t lp = L > 0 ? (L + want - 1) / want : 1;
+  if (lp < kMinPiece) lp = kMinPiece;
+  // the scan addresses a piece through 32-bit byte offsets: keep each piece's rows under 2 GiB
+  const int64_t max_rows = ((int64_t)1 << 31) / row_bytes - 1;
+  if (lp > max_rows) lp = max_rows;
+  *Lp = (int)(lp < L ? lp : (L > 0 ? L : 1));
+  *P = L > 0 ? (int)((L + *Lp - 1) / *Lp) : 1;
+}
 
 int64_t mixer_workspace_bytes(const jm_mixer_dims* dims, bool decode, bool varlen) {
   const int s = check_dims(dims, decode);

@@ -440,6 +440,21 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
 
 }  // namespace
 
+void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st) {
+  if (a.P <= 1) return;
+  const int64_t n = (int64_t)a.B * kN * a.C;
+  dim3 gl(a.C / 64, a.P - 1, a.B);
+  if (bf16) {
+    hipLaunchKernelGGL((scan_pass_kernel<bf16_t, false, false>), gl, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((scan_carry_kernel<bf16_t, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.loc,
+                       (const bf16_t*)a.A_log, a.h0, a.cin, a.B, a.C, a.P, a);
+  } else {
+    hipLaunchKernelGGL((scan_pass_kernel<float, false, false>), gl, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((scan_carry_kernel<float, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.loc,
+                       (const float*)a.A_log, a.h0, a.cin, a.B, a.C, a.P, a);
+  }
+}
+
 void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks) {
   if (a.cu) {
     if (bf16) run_scan<bf16_t, true>(a, st, marks);

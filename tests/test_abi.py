@@ -198,3 +198,31 @@ def test_varlen_prefill_validation_before_launch():
     assert lcall(cu=None) == _lib.JM_ERR_INVALID_ARG
     assert lcall(cu=FAKE + 2) == _lib.JM_ERR_ALIGNMENT
     assert lcall(ws_bytes=16) == _lib.JM_ERR_WORKSPACE
+
+
+def test_scan_train_validation_before_launch():
+    d = jm.scan_dims(2, 64, 128, jm.JM_BF16)
+    L = _lib.lib()
+    nf, nb = jm.scan_workspace_size(d), jm.scan_workspace_size(d, True)
+    assert nf > 0 and nb > 0
+    assert jm.scan_workspace_size(jm.scan_dims(2, 64, 96, jm.JM_BF16)) == 0                 # d_inner % 64
+    assert jm.scan_workspace_size(jm.scan_dims(2, 64, 128, jm.JM_BF16, d_state=8), True) == 0
+    assert jm.scan_workspace_size(jm.scan_dims(2, (1 << 21) + 1, 128, jm.JM_BF16)) == 0
+    fwd = lambda dims, ws_bytes=WS_BIG, x=FAKE, h_out=FAKE: L.jm_scan_forward(
+        ctypes.byref(dims), x, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, h_out, FAKE, ws_bytes, None)
+    assert fwd(d, x=None) == _lib.JM_ERR_INVALID_ARG
+    assert fwd(d, h_out=None) == _lib.JM_ERR_INVALID_ARG
+    assert fwd(d, x=FAKE + 4) == _lib.JM_ERR_ALIGNMENT
+    assert fwd(d, ws_bytes=nf - 1) == _lib.JM_ERR_WORKSPACE
+    assert fwd(jm.scan_dims(0, 64, 128, jm.JM_BF16)) == _lib.JM_ERR_INVALID_ARG
+    bwd = lambda dims, ws_bytes=WS_BIG, dx=FAKE, dA=FAKE, dout=FAKE: L.jm_scan_backward(
+        ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, dout, None, dx, FAKE, FAKE, FAKE, dA, FAKE,
+        None, FAKE, ws_bytes, None)
+    assert bwd(d, dx=None) == _lib.JM_ERR_INVALID_ARG
+    assert bwd(d, dA=None) == _lib.JM_ERR_INVALID_ARG
+    assert bwd(d, dout=FAKE + 8) == _lib.JM_ERR_ALIGNMENT
+    assert bwd(d, ws_bytes=nb - 1) == _lib.JM_ERR_WORKSPACE
+    # no tokens: the activations may be NULL; only the parameter gradients are required
+    e = jm.scan_dims(2, 0, 128, jm.JM_BF16)
+    assert L.jm_scan_backward(ctypes.byref(e), None, None, None, None, FAKE, FAKE, None, None, None, None, None,
+                              None, None, FAKE, FAKE, None, FAKE, 0, None) == _lib.JM_ERR_WORKSPACE
