@@ -9,7 +9,8 @@ device synchronisations; value = tokens / second.  A second timed pass records H
 library's kernels (jm_mixer_prefill_profiled) for the per-kernel roofline.  The decode workload (B=256,
 one token per sequence, the fp32 state rotated over 4 sets so that it streams from HBM) is timed the same
 way and reported alongside, as are the whole Mamba layer around the mixer and the serving-style calls
-(a packed batch of prompts of mixed lengths, decode over a state pool).  The fp64 CPU oracle is timed on the host on the same prefill workload as a
+(a packed batch of prompts of mixed lengths, decode over a state pool) and the gated scan's training
+forward and backward.  The fp64 CPU oracle is timed on the host on the same prefill workload as a
 baseline.
 
 Prints one JSON line.  Only one GPU is supported: --gpus N with N > 1 exits with a message.
@@ -93,6 +94,19 @@ def scan_alu_ops(B, L, C, N):
     and SiLU's multiply, add and multiply = 6 operations + 2 transcendentals (exp, reciprocal)."""
     tc = B * L * C
     ops = tc * N * 4 + tc * 6
+    trans = tc * N + tc * 2
+    return ops + TRANS_SLOTS * trans
+
+
+def scan_bwd_alu_ops(B, L, C, N):
+    """fp32 VALU work of the scan's backward as the chain rule defines it, in full-rate issue slots, with the
+    forward states recomputed (they are not kept between the two calls).  Per (token, channel, state): the
+    state's recurrence again (delta*A, its exponential, (delta*x)*B, the FMA: 3 operations + 1 transcendental)
+    and the reverse step (g = u + C*dy, g*h*a, the d delta terms, g*delta, d B, d x, d A, d C, C.h for y and
+    u = a*g: 13 operations, reusing the exponential).  Per (token, channel): sigmoid(z) (exp, reciprocal),
+    SiLU and its derivative, dy, dz, the D terms and d D: 11 operations + 2 transcendentals."""
+    tc = B * L * C
+    ops = tc * N * 16 + tc * 11
     trans = tc * N + tc * 2
     return ops + TRANS_SLOTS * trans
 
@@ -436,6 +450,65 @@ def time_serving(jm, steps, warmup):
     return res
 
 
+def time_training(jm, steps, warmup):
+    """The gated scan alone at the 4K prefill's shape (B=1, L=4096, d_inner 8192, bf16): its training forward
+    (jm_scan_forward) and backward (jm_scan_backward), timed separately."""
+    import torch
+    from jm_inputs import CONFIGS, make_scan_problem
+
+    cfg = CONFIGS[1].replace(name="jamba_scan_train_B1_L4096", seed=1301)
+    p = make_scan_problem(cfg, "cuda")
+    B, L, C, N = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state
+    dims = jm.scan_dims(B, L, C, jm.JM_BF16)
+    L_ = jm.lib()
+    wsf = torch.empty(jm.scan_workspace_size(dims), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(jm.scan_workspace_size(dims, True), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(p["x"])
+    h_out = torch.empty((B, C, N), dtype=torch.float32, device="cuda")
+    g = {k: torch.empty_like(p["x"]) for k in ("dx", "ddelta", "dz")}
+    dbc = torch.empty((B * L, 2 * N), dtype=torch.float32, device="cuda")
+    dA = torch.empty((C, N), dtype=torch.float32, device="cuda")
+    dD = torch.empty((C,), dtype=torch.float32, device="cuda")
+    dh0 = torch.empty((B, C, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+
+    def fwd(i):
+        s = L_.jm_scan_forward(ctypes.byref(dims), ptr(p["x"]), ptr(p["delta"]), ptr(p["z"]), ptr(p["bc"]),
+                               ptr(p["A_log"]), ptr(p["D"]), ptr(p["h0"]), ptr(out), ptr(h_out), ptr(wsf), wsf.numel(),
+                               stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_scan_forward")
+
+    def bwd(i):
+        s = L_.jm_scan_backward(ctypes.byref(dims), ptr(p["x"]), ptr(p["delta"]), ptr(p["z"]), ptr(p["bc"]),
+                                ptr(p["A_log"]), ptr(p["D"]), ptr(p["h0"]), ptr(p["dout"]), ptr(p["dh_final"]),
+                                ptr(g["dx"]), ptr(g["ddelta"]), ptr(g["dz"]), ptr(dbc), ptr(dA), ptr(dD), ptr(dh0),
+                                ptr(wsb), wsb.numel(), stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_scan_backward")
+
+    res = {"workload": f"{cfg.name}: the gated scan alone, B={B} L={L} d_inner={C}, bf16 I/O, fp32 state"}
+    for name, step in (("forward", fwd), ("backward", bwd)):
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        ops = scan_alu_ops(B, L, C, N) if name == "forward" else scan_bwd_alu_ops(B, L, C, N)
+        ach = ops / (ms * 1e-3) / 1e12
+        res[name] = {"us": round(ms * 1e3, 2), "tokens_per_s": round(B * L / (ms * 1e-3), 1),
+                     "alg_ops": ops, "T_lane_ops_s": round(ach, 2), "frac_alu": round(ach / VALU_PEAK_TOPS, 4)}
+        log(f"  scan {name}: {ms * 1e3:.1f} us")
+    res["backward_over_forward"] = round(res["backward"]["us"] / res["forward"]["us"], 2)
+    return res
+
+
 def run_decode(jm, dcfg, args, hip):
     log(f"decode {dcfg.name}: warmup {args.warmup}, steps {args.steps}")
     dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
@@ -462,6 +535,10 @@ def main():
     ap.add_argument("--config", type=int, default=1, choices=(1, 2, 3),
                     help="prefill workload: 1 = B1 L4096 (default), 2 = B8 L4096, 3 = B1 L262144")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the gated scan's training forward / backward timing")
+    ap.add_argument("--training-only", action="store_true",
+                    help="time only the scan's training forward / backward (for per-kernel profiles)")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the serving-style timings (packed prefill, pooled-state decode)")
     ap.add_argument("--decode-only", action="store_true",
@@ -494,6 +571,9 @@ def main():
         del src, dst
     if args.decode_only:
         print(json.dumps({"decode": run_decode(jm, CONFIGS[4], args, hip)}), flush=True)
+        return
+    if args.training_only:
+        print(json.dumps({"training": time_training(jm, args.steps, args.warmup)}), flush=True)
         return
     cfg = CONFIGS[args.config]
     log(f"prefill {cfg.name}: warmup {args.warmup}, steps {args.steps}")
@@ -577,6 +657,9 @@ def main():
         if "decode" in result:
             result["serving"]["decode_slots"]["vs_plain_decode"] = round(
                 result["decode"]["us_per_step"] / result["serving"]["decode_slots"]["us_per_step"], 3)
+    if not args.no_training and args.config == 1:
+        log(f"training (scan forward / backward): warmup {args.warmup}, steps {args.steps}")
+        result["training"] = time_training(jm, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {min(args.cpu_tokens, cfg.seqlen)} tokens ...")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)

@@ -99,7 +99,10 @@ void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st);
 void scan_plan(int B, int L, int C, int64_t row_bytes, int* P, int* Lp);
 
 // Backward of the gated scan (training).  Pieces of kBwdPiece tokens; all [B*L, C] tensors contiguous.
-constexpr int kBwdPiece = 128;
+#ifndef JM_BWD_PIECE
+#define JM_BWD_PIECE 32
+#endif
+constexpr int kBwdPiece = JM_BWD_PIECE;
 struct BwdArgs {
   const void* xc;        // [B*L, C] io dtype
   const void* delta;     // [B*L, C]

@@ -29,16 +29,34 @@ namespace {
 
 constexpr int kN = 16;
 constexpr int kQ = 4;                  // states per lane
-constexpr int kSub = 16;               // tokens per recomputed sub-chunk
+// Tile sizes measured at B=1, L=4096, d_inner 8192 (bf16): sub-chunks of 4 tokens in pieces of 32 at four
+// waves per SIMD took 1073 us for the whole backward, against 1106 (8 / 64, two waves), 1174 (4 / 16) and
+// 1244 (8 / 32, three waves); keeping the decay factors and prefetching every input won over recomputing.
+#ifndef JM_BWD_SUB
+#define JM_BWD_SUB 4
+#endif
+#ifndef JM_BWD_WAVES_PER_SIMD
+#define JM_BWD_WAVES_PER_SIMD 4
+#endif
+#ifndef JM_BWD_KEEP_E
+#define JM_BWD_KEEP_E 1
+#endif
+#ifndef JM_BWD_PREFETCH_ZO
+#define JM_BWD_PREFETCH_ZO 1
+#endif
+constexpr int kSub = JM_BWD_SUB;       // tokens per recomputed sub-chunk
+constexpr int kBwdWavesPerSimd = JM_BWD_WAVES_PER_SIMD;   // the second __launch_bounds__ argument
 constexpr int kPiece = kBwdPiece;      // tokens per piece (a multiple of kSub)
 constexpr int kNSub = kPiece / kSub;
 static_assert(kPiece % kSub == 0, "pieces hold whole sub-chunks");
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
+// v read from another lane of the same row (every lane valid for these controls); as a plain DPP move with
+// full masks the compiler folds it into the add that consumes it (v_add_f32 with a DPP source)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 // sum over the four lanes of a quad (the four state groups of one channel), in every lane
 __device__ __forceinline__ float quad_sum(float v) {
@@ -79,39 +97,100 @@ __device__ __forceinline__ void st4(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
+// One channel's column of a [rows, C] io-dtype tensor over a piece's rows, through a raw buffer resource:
+// the lane's channel is the vector offset and the token row a wave-uniform scalar offset, so a load or
+// store needs no per-lane address arithmetic.
+constexpr int kBufFlags = 0x00020000;   // dword 3 of a raw buffer descriptor on gfx9-family GPUs
+template <typename T>
+struct Col {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t voff, row_bytes;
+  __device__ __forceinline__ Col(const void* base, int64_t row0, int rows, int C, int c) {
+    const int64_t bytes = (int64_t)(rows > 0 ? rows : 1) * C * sizeof(T);
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>((const T*)base + row0 * C), (short)0, (int)bytes,
+                                          kBufFlags);
+    voff = (uint32_t)c * sizeof(T);
+    row_bytes = (uint32_t)C * sizeof(T);
+  }
+  __device__ __forceinline__ float ld(int i) const;
+  __device__ __forceinline__ void st(int i, float v) const;
+};
+template <>
+__device__ __forceinline__ float Col<bf16_t>::ld(int i) const {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, (uint32_t)i * row_bytes, 0) << 16);
+}
+template <>
+__device__ __forceinline__ void Col<bf16_t>::st(int i, float v) const {
+  __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), r, voff, (uint32_t)i * row_bytes, 0);
+}
+template <>
+__device__ __forceinline__ float Col<float>::ld(int i) const {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, (uint32_t)i * row_bytes, 0));
+}
+template <>
+__device__ __forceinline__ void Col<float>::st(int i, float v) const {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, (uint32_t)i * row_bytes, 0);
+}
+
 // Backward local pass: pieces 1 .. P-1 run the gradient recurrence from zero at their end and record
 // u at their first token (what flows into the previous piece) and their delta sum:
-// bloc [B, P, N + 1, C] (state n at row n, the delta sum at row N).
+// bloc [B, P, N + 1, C] (state n at row n, the delta sum at row N).  Only the recurrence of u runs here, so a
+// lane takes a whole channel (all 16 states), and the piece's C rows, shared by every channel, are read from
+// LDS as broadcasts.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a) {
-  const Lane l = lane_of();
+__global__ __launch_bounds__(64) void bwd_local_kernel(BwdArgs a) {
+  const int c = blockIdx.x * 64 + threadIdx.x;
   const int p = blockIdx.y + 1;
   const int b = blockIdx.z;
   const int C = a.C, L = a.L, P = a.P;
   const int t0 = p * kPiece, t1 = min(L, t0 + kPiece);
-  float A[kQ], a2[kQ];
-  load_A((const T*)a.A_log, l, A, a2);
-  const int64_t row0 = (int64_t)b * L;
-  float u[kQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int n_tok = t1 - t0;
+  const int64_t row0 = (int64_t)b * L + t0;
+  __shared__ f32x4 sc[kPiece][kN / 4];
+  for (int o = threadIdx.x; o < n_tok * (kN / 4); o += 64)
+    sc[o / (kN / 4)][o % (kN / 4)] = ld4(a.bc + (row0 + o / (kN / 4)) * (2 * kN) + kN + (o % (kN / 4)) * 4);
+  float a2[kN];
+#pragma unroll
+  for (int n = 0; n < kN; ++n) a2[n] = -exp2_fast(io<T>::ld((const T*)a.A_log + (int64_t)c * kN + n) * kLog2e) * kLog2e;
+  const Col<T> dl(a.delta, row0, n_tok, C, c), zl(a.z, row0, n_tok, C, c), ol(a.dout, row0, n_tok, C, c);
+  __syncthreads();
+  float u[kN];
+#pragma unroll
+  for (int n = 0; n < kN; ++n) u[n] = 0.0f;
   float sdt = 0.0f;
-  for (int t = t1 - 1; t >= t0; --t) {
-    const int64_t r = row0 + t;
-    const float d = io<T>::ld((const T*)a.delta + r * C + l.c);
-    const float zv = io<T>::ld((const T*)a.z + r * C + l.c);
-    const float dout = io<T>::ld((const T*)a.dout + r * C + l.c);
-    const f32x4 Cv = ld4(a.bc + r * (2 * kN) + kN + l.q * kQ);
-    const float dy = dout * silu(zv);
+  // tokens last to first in batches whose loads are all issued first (indices clamped to the piece)
+  constexpr int kBatch = 8;
+  for (int ib = n_tok - 1; ib >= 0; ib -= kBatch) {
+    float dd[kBatch], dy[kBatch];
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-      const float g = fmaf(Cv[i], dy, u[i]);
-      u[i] = exp2_fast(d * a2[i]) * g;
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = max(ib - j, 0);
+      dd[j] = dl.ld(i);
+      dy[j] = zl.ld(i);
     }
-    sdt += d;
-  }
-  float* dst = a.bloc + ((int64_t)b * P + p) * (kN + 1) * C + l.c;
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) dst[(int64_t)(l.q * kQ + i) * C] = u[i];
-  if (l.q == 0) dst[(int64_t)kN * C] = sdt;
+    for (int j = 0; j < kBatch; ++j) dy[j] = ol.ld(max(ib - j, 0)) * silu(dy[j]);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (ib - j >= 0) {
+        const int i = ib - j;
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q) {
+          const f32x4 Cv = sc[i][q];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int n = q * 4 + s;
+            u[n] = exp2_fast(dd[j] * a2[n]) * fmaf(Cv[s], dy[j], u[n]);
+          }
+        }
+        sdt += dd[j];
+      }
+    }
+  }
+  float* dst = a.bloc + ((int64_t)b * P + p) * (kN + 1) * C + c;
+#pragma unroll
+  for (int n = 0; n < kN; ++n) dst[(int64_t)n * C] = u[n];
+  dst[(int64_t)kN * C] = sdt;
 }
 
 // Backward carry: per (b, n, c), the gradient entering each piece from later tokens:
@@ -153,8 +232,10 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
 //   pA [B*P, C, N]  per-piece sums of g h_{t-1} a delta (d A before the factor A)
 //   pD [B*P, C]     per-piece sums of dy x
 //   pbc [C/64, B*L, 2N]  per-block sums over its 64 channels of d B (columns 0..N-1) and d C (N..2N-1)
+// B / C of the piece (shared by every channel) are staged in LDS once; the per-channel inputs of the next
+// sub-chunk are loaded while the current one computes (indices clamped, so no load is conditional).
 template <typename T>
-__global__ __launch_bounds__(256, 2) void bwd_full_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs a) {
   const Lane l = lane_of();
   const int p = blockIdx.y;
   const int b = blockIdx.z;
@@ -165,17 +246,19 @@ __global__ __launch_bounds__(256, 2) void bwd_full_kernel(BwdArgs a) {
   const int64_t row0 = (int64_t)b * L + t0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  __shared__ __attribute__((aligned(16))) float ck[kNSub][256][kQ];       // state at each sub-chunk start
-  __shared__ float red[kSub][16][2 * kQ * 4 + 1];                          // per-row d B / d C sums (+1 pad)
+  __shared__ f32x4 ck[kNSub][256];                 // state at each sub-chunk start, per lane
+  __shared__ f32x4 red[kSub][16][2 * kQ + 1];      // per-row d B / d C sums (4 x B, 4 x C float4, + pad)
+  __shared__ f32x4 sbc[kPiece][2 * kQ];            // B (4 x float4) then C (4 x float4) of each token
+
+  for (int o = threadIdx.x; o < n_tok * 2 * kQ; o += 256)
+    sbc[o / (2 * kQ)][o % (2 * kQ)] = ld4(a.bc + row0 * (2 * kN) + (int64_t)o * 4);
 
   float A[kQ], a2[kQ];
   load_A((const T*)a.A_log, l, A, a2);
   const float Dc = io<T>::ld((const T*)a.D + l.c);
-  const T* dl = (const T*)a.delta + row0 * C + l.c;
-  const T* xl = (const T*)a.xc + row0 * C + l.c;
-  const T* zl = (const T*)a.z + row0 * C + l.c;
-  const T* ol = (const T*)a.dout + row0 * C + l.c;
-  const float* bcl = a.bc + row0 * (2 * kN) + l.q * kQ;
+  const Col<T> dl(a.delta, row0, n_tok, C, l.c), xl(a.xc, row0, n_tok, C, l.c), zl(a.z, row0, n_tok, C, l.c),
+      ol(a.dout, row0, n_tok, C, l.c);
+  const Col<T> gdd(a.ddelta, row0, n_tok, C, l.c), gdx(a.dxc, row0, n_tok, C, l.c), gdz(a.dz, row0, n_tok, C, l.c);
 
   // incoming state and incoming gradient of the piece
   float h[kQ], u[kQ];
@@ -193,52 +276,107 @@ __global__ __launch_bounds__(256, 2) void bwd_full_kernel(BwdArgs a) {
       }
     }
   }
+  auto load2 = [&](int k, float* d, float* x) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      const int i = min(k * kSub + j, n_tok - 1);
+      d[j] = dl.ld(i);
+      x[j] = xl.ld(i);
+    }
+  };
+  auto load2zo = [&](int k, float* z, float* o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      const int i = min(k * kSub + j, n_tok - 1);
+      z[j] = zl.ld(i);
+      o[j] = ol.ld(i);
+    }
+  };
+  __syncthreads();   // sbc
 
   // forward through the piece, saving the state at each sub-chunk start
-  for (int k = 0; k < nsub; ++k) {
-    *reinterpret_cast<f32x4*>(&ck[k][threadIdx.x][0]) = f32x4{h[0], h[1], h[2], h[3]};
-    const int j1 = min(kSub, n_tok - k * kSub);
-    for (int j = 0; j < j1; ++j) {
-      const int i = k * kSub + j;
-      const float d = io<T>::ld(dl + (int64_t)i * C);
-      const float dx = d * io<T>::ld(xl + (int64_t)i * C);
-      const f32x4 Bv = ld4(bcl + (int64_t)i * (2 * kN));
+  {
+    float dn[kSub], xn[kSub];
+    load2(0, dn, xn);
+    for (int k = 0; k < nsub; ++k) {
+      ck[k][threadIdx.x] = f32x4{h[0], h[1], h[2], h[3]};
+      float dd[kSub], xx[kSub];
 #pragma unroll
-      for (int s = 0; s < kQ; ++s) h[s] = fmaf(exp2_fast(d * a2[s]), h[s], dx * Bv[s]);
+      for (int j = 0; j < kSub; ++j) {
+        dd[j] = dn[j];
+        xx[j] = xn[j];
+      }
+      load2(min(k + 1, nsub - 1), dn, xn);
+      const int j1 = min(kSub, n_tok - k * kSub);
+#pragma unroll
+      for (int j = 0; j < kSub; ++j) {
+        if (j < j1) {
+          const f32x4 Bv = sbc[k * kSub + j][l.q];
+          const float dx = dd[j] * xx[j];
+#pragma unroll
+          for (int s = 0; s < kQ; ++s) h[s] = fmaf(exp2_fast(dd[j] * a2[s]), h[s], dx * Bv[s]);
+        }
+      }
     }
   }
 
   float dA[kQ] = {0.0f, 0.0f, 0.0f, 0.0f};
   float dD = 0.0f;
+  float pd[kSub], px[kSub];   // the next sub-chunk's per-channel inputs
+  load2(nsub - 1, pd, px);
+#if JM_BWD_PREFETCH_ZO
+  float pz[kSub], po[kSub];
+  load2zo(nsub - 1, pz, po);
+#endif
   for (int k = nsub - 1; k >= 0; --k) {
     const int len = min(kSub, n_tok - k * kSub);
-    // recompute the sub-chunk's states: hist[j] = state after its token j; keep delta, x and the gate terms
-    float hist[kSub][kQ], dv[kSub], xv[kSub], dyv[kSub], dzf[kSub];
-    float hs[kQ];
-    {
-      const f32x4 c4 = *reinterpret_cast<const f32x4*>(&ck[k][threadIdx.x][0]);
+    float dv[kSub], xv[kSub], dyv[kSub], dzf[kSub];
+#if JM_BWD_PREFETCH_ZO
 #pragma unroll
-      for (int s = 0; s < kQ; ++s) hs[s] = c4[s];
+    for (int j = 0; j < kSub; ++j) {
+      dyv[j] = pz[j];
+      dzf[j] = po[j];
     }
+    load2zo(max(k - 1, 0), pz, po);
+#else
+    load2zo(k, dyv, dzf);
+#endif
 #pragma unroll
-    for (int s = 0; s < kQ; ++s) h[s] = hs[s];
+    for (int j = 0; j < kSub; ++j) {
+      dv[j] = pd[j];
+      xv[j] = px[j];
+    }
+    load2(max(k - 1, 0), pd, px);
+    // recompute the sub-chunk's states: hist[j] = state after its token j, ehist[j] its decay factors; the
+    // gate terms
+    float hist[kSub][kQ];
+#if JM_BWD_KEEP_E
+    float ehist[kSub][kQ];
+#endif
+    const f32x4 c4 = ck[k][threadIdx.x];
+    float hs[kQ];
+#pragma unroll
+    for (int s = 0; s < kQ; ++s) {
+      hs[s] = c4[s];
+      h[s] = c4[s];
+    }
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
       if (j < len) {
-        const int i = k * kSub + j;
-        const float d = io<T>::ld(dl + (int64_t)i * C);
-        const float x = io<T>::ld(xl + (int64_t)i * C);
-        const float zv = io<T>::ld(zl + (int64_t)i * C);
-        const float dout = io<T>::ld(ol + (int64_t)i * C);
-        const f32x4 Bv = ld4(bcl + (int64_t)i * (2 * kN));
+        const f32x4 Bv = sbc[k * kSub + j][l.q];
+        const float d = dv[j], x = xv[j];
+        const float dx = d * x;
 #pragma unroll
         for (int s = 0; s < kQ; ++s) {
-          h[s] = fmaf(exp2_fast(d * a2[s]), h[s], d * x * Bv[s]);
+          const float e = exp2_fast(d * a2[s]);
+#if JM_BWD_KEEP_E
+          ehist[j][s] = e;
+#endif
+          h[s] = fmaf(e, h[s], dx * Bv[s]);
           hist[j][s] = h[s];
         }
+        const float zv = dyv[j], dout = dzf[j];
         const float sg = rcp_fast(1.0f + exp2_fast(-zv * kLog2e));   // sigmoid(z)
-        dv[j] = d;
-        xv[j] = x;
         dyv[j] = dout * zv * sg;                                     // dout * SiLU(z)
         dzf[j] = dout * sg * fmaf(zv, 1.0f - sg, 1.0f);              // dout * SiLU'(z)
       }
@@ -248,33 +386,37 @@ __global__ __launch_bounds__(256, 2) void bwd_full_kernel(BwdArgs a) {
     for (int j = kSub - 1; j >= 0; --j) {
       if (j < len) {
         const int i = k * kSub + j;
-        const f32x4 Bv = ld4(bcl + (int64_t)i * (2 * kN));
-        const f32x4 Cv = ld4(bcl + (int64_t)i * (2 * kN) + kN);
+        const f32x4 Bv = sbc[i][l.q], Cv = sbc[i][kQ + l.q];
         const float d = dv[j], x = xv[j], dy = dyv[j];
-        float pdd = 0.0f, pdx = 0.0f, py = 0.0f;
+        const float dx = d * x;
+        // per state: g, sum g B (-> d delta's B x term and d x), g h_{t-1} a (-> d delta's A term and d A)
+        float gB = 0.0f, pdA = 0.0f, py = 0.0f;
         float vb[kQ], vc[kQ];
 #pragma unroll
         for (int s = 0; s < kQ; ++s) {
           const float hp = j > 0 ? hist[j > 0 ? j - 1 : 0][s] : hs[s];
+#if JM_BWD_KEEP_E
+          const float e = ehist[j][s];
+#else
           const float e = exp2_fast(d * a2[s]);
+#endif
           const float g = fmaf(Cv[s], dy, u[s]);
+          gB = fmaf(g, Bv[s], gB);
           const float ghe = g * hp * e;
-          pdd = fmaf(ghe, A[s], fmaf(g * Bv[s], x, pdd));
-          pdx = fmaf(g * d, Bv[s], pdx);
+          pdA = fmaf(ghe, A[s], pdA);
           dA[s] = fmaf(ghe, d, dA[s]);
-          vb[s] = g * d * x;
+          vb[s] = g * dx;
           vc[s] = dy * hist[j][s];
           py = fmaf(Cv[s], hist[j][s], py);
           u[s] = e * g;
         }
-        pdd = quad_sum(pdd);
-        pdx = quad_sum(pdx);
+        gB = quad_sum(gB);
+        pdA = quad_sum(pdA);
         py = quad_sum(py);
         if (l.q == 0) {
-          const int64_t r = (row0 + i) * C + l.c;
-          io<T>::st((T*)a.ddelta + r, pdd);
-          io<T>::st((T*)a.dxc + r, fmaf(Dc, dy, pdx));
-          io<T>::st((T*)a.dz + r, fmaf(Dc, x, py) * dzf[j]);
+          gdd.st(i, fmaf(gB, x, pdA));
+          gdx.st(i, fmaf(Dc, dy, gB * d));
+          gdz.st(i, fmaf(Dc, x, py) * dzf[j]);
         }
         dD = fmaf(dy, x, dD);
         // d B / d C of this token summed over the row's four channels; lanes 0..3 of each row keep them
@@ -284,12 +426,8 @@ __global__ __launch_bounds__(256, 2) void bwd_full_kernel(BwdArgs a) {
           vc[s] = row_q_sum(vc[s]);
         }
         if ((lane & 15) < 4) {
-          float* rr = &red[j][wave * 4 + (lane >> 4)][l.q * 2 * kQ];
-#pragma unroll
-          for (int s = 0; s < kQ; ++s) {
-            rr[s] = vb[s];
-            rr[kQ + s] = vc[s];
-          }
+          red[j][wave * 4 + (lane >> 4)][l.q * 2] = f32x4{vb[0], vb[1], vb[2], vb[3]};
+          red[j][wave * 4 + (lane >> 4)][l.q * 2 + 1] = f32x4{vc[0], vc[1], vc[2], vc[3]};
         }
       }
     }
@@ -297,12 +435,12 @@ __global__ __launch_bounds__(256, 2) void bwd_full_kernel(BwdArgs a) {
     // sum the block's 16 rows and write this block's partial d B / d C for the sub-chunk's tokens
     for (int o = threadIdx.x; o < len * 2 * kN; o += 256) {
       const int j = o / (2 * kN), col = o % (2 * kN);
-      // column col: d B (col < N) or d C of state n = col % N, held by state group n / 4 at slot n % 4
+      // column col: d B (col < N) or d C of state n = col % N, held by state group n / 4, element n % 4
       const int n = col % kN, q = n / kQ;
-      const int slot = q * 2 * kQ + (col < kN ? 0 : kQ) + n % kQ;
+      const float* base = reinterpret_cast<const float*>(&red[j][0][q * 2 + (col < kN ? 0 : 1)]) + n % kQ;
       float sum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += red[j][r][slot];
+      for (int r = 0; r < 16; ++r) sum += base[r * (2 * kQ + 1) * 4];
       a.pbc[((int64_t)blockIdx.x * a.B * L + row0 + k * kSub + j) * (2 * kN) + col] = sum;
     }
     __syncthreads();
@@ -320,8 +458,17 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
                                                             int64_t rows, int nblk) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over rows * 2N
   if (i >= rows * 2 * kN) return;
+  // eight loads in flight per step (the partials are summed in block order)
   float s = 0.0f;
-  for (int k = 0; k < nblk; ++k) s += pbc[(int64_t)k * rows * 2 * kN + i];
+  int k = 0;
+  for (; k + 8 <= nblk; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = pbc[(int64_t)(k + j) * rows * 2 * kN + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; k < nblk; ++k) s += pbc[(int64_t)k * rows * 2 * kN + i];
   dbc[i] = s;
 }
 
@@ -332,21 +479,29 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __r
                                                                 float* __restrict__ dD, int C, int npieces) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;   // over C * N
   if (i >= C * kN) return;
-  float s = 0.0f;
-  for (int k = 0; k < npieces; ++k) s += pA[(int64_t)k * C * kN + i];
+  // eight loads in flight per step (the partials are summed in piece order)
+  auto sum = [&](const float* part, int64_t stride) __attribute__((always_inline)) {
+    float s = 0.0f;
+    int k = 0;
+    for (; k + 8 <= npieces; k += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(int64_t)(k + j) * stride + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; k < npieces; ++k) s += part[(int64_t)k * stride + i];
+    return s;
+  };
   const float A = -exp2_fast(io<T>::ld(A_log + i) * kLog2e);
-  dA_log[i] = s * A;
-  if (i < C) {
-    float sd = 0.0f;
-    for (int k = 0; k < npieces; ++k) sd += pD[(int64_t)k * C + i];
-    dD[i] = sd;
-  }
+  dA_log[i] = sum(pA, (int64_t)C * kN) * A;
+  if (i < C) dD[i] = sum(pD, C);
 }
 
 template <typename T>
 void run_bwd(const BwdArgs& a, hipStream_t st) {
   if (a.P > 1) {
-    hipLaunchKernelGGL(bwd_local_kernel<T>, dim3(a.C / 64, a.P - 1, a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_local_kernel<T>, dim3(a.C / 64, a.P - 1, a.B), dim3(64), 0, st, a);
     const int64_t n = (int64_t)a.B * kN * a.C;
     hipLaunchKernelGGL(bwd_carry_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   }

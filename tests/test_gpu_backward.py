@@ -2,8 +2,8 @@
 
 The backward's gradients are sums (over tokens for dA_log and dD, over channels for dB and dC), so they are
 compared relative to their largest magnitude: fp32 within 1e-4 * max(1, max |ref|), bf16 within 2e-2 of
-max |ref| (the bf16 I/O tolerance of the forward).  Cases span several 128-token pieces, ragged sub-chunks
-and pieces, a single short piece, no initial state, no tokens, and Jamba's widths at 1024 tokens.
+max |ref| (the bf16 I/O tolerance of the forward).  Cases span many 32-token pieces, ragged sub-chunks and
+pieces, a single short piece, no initial state, no tokens, and Jamba's widths at 1024 tokens.
 """
 
 import numpy as np
@@ -54,7 +54,7 @@ def _check_backward(cfg, with_state=True):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_scan_backward_pieces_and_ragged_tail(io):
-    # 300 tokens: pieces of 128, 128 and 44 tokens (the last with a ragged 16-token sub-chunk)
+    # 300 tokens: nine full 32-token pieces and a ragged last piece of 12 (its sub-chunks ragged too)
     cfg = MixerConfig(f"scan_bwd_{io}", batch=2, seqlen=300, d_inner=128, io_dtype=io, seed=61)
     _check_backward(cfg)
 
