@@ -33,17 +33,18 @@ __all__ = ["layer_prefill", "layer_decode_step"]
 def layer_prefill(x_res: np.ndarray, lw: Dict[str, np.ndarray], w: Dict[str, np.ndarray], dt_rank: int,
                   d_state: int, eps: float = 1e-6, layer_eps: float = 1e-6,
                   conv_state: Optional[np.ndarray] = None, ssm_state: Optional[np.ndarray] = None,
-                  return_intermediates: bool = False):
+                  return_intermediates: bool = False, zoh: bool = False):
     """The layer from the residual stream x_res [B, L, d_model] to x_res + out_proj(mixer(...)).
 
     ``lw`` holds norm_w [d_model], in_proj_w [2 C, d_model], out_proj_w [d_model, C]; ``w`` the mixer's
-    weights.  Returns (out, conv_state_out, ssm_state_out[, intermediates]).
+    weights; ``zoh`` selects the mixer's exact zero-order-hold variant.  Returns (out, conv_state_out,
+    ssm_state_out[, intermediates]).
     """
     C = w["D"].shape[0]
     hn = rms_norm(x_res, lw["norm_w"], layer_eps)
     xz = hn @ lw["in_proj_w"].T
     x, z = xz[..., :C], xz[..., C:]
-    y, conv_out, h = mixer_prefill(x, z, w, dt_rank, d_state, eps, conv_state, ssm_state)
+    y, conv_out, h = mixer_prefill(x, z, w, dt_rank, d_state, eps, conv_state, ssm_state, zoh=zoh)
     out = x_res + y @ lw["out_proj_w"].T
     if not return_intermediates:
         return out, conv_out, h

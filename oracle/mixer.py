@@ -23,7 +23,8 @@ Every step is the plain definition, written out in float64 numpy, in the order t
 
 Readings where the pages leave a step open (each is listed with its reason in the design notes): the D skip,
 the conv bias and the SiLU after the conv, and the z gate are not on the pages and follow the mixer's
-conventional form; B is discretised as dt*B (the pages' own approximation), not exact ZOH; the norms apply
+conventional form; B is discretised as dt*B (the pages' own approximation) by default, with the exact ZOH
+form the pages print beside it as an option; the norms apply
 to the dt slice before dt_proj; rms_norm(v) = v / sqrt(mean(v^2) + eps) * w; the conv state holds the last
 K-1 raw inputs, oldest first; the SSM state is fp32 on the device and fp64 here.
 
@@ -101,13 +102,16 @@ def dt_proj_softplus(dln: np.ndarray, dt_proj_w: np.ndarray, dt_proj_b: np.ndarr
 
 
 def selective_scan(xc: np.ndarray, delta: np.ndarray, A_log: np.ndarray, Bn: np.ndarray, Cn: np.ndarray,
-                   D: np.ndarray, h0: Optional[np.ndarray]):
+                   D: np.ndarray, h0: Optional[np.ndarray], zoh: bool = False):
     """The selective scan, one token at a time.
 
     xc, delta [B, L, C]; A_log [C, N]; Bn, Cn [B, L, N] (shared by all channels); D [C];
     h0 [B, C, N] or None (zeros).  With A = -exp(A_log), for t = 0 .. L-1:
-        h[b, c, n] <- exp(delta[b,t,c] * A[c,n]) * h[b, c, n] + delta[b,t,c] * Bn[b,t,n] * xc[b,t,c]
+        h[b, c, n] <- exp(delta[b,t,c] * A[c,n]) * h[b, c, n] + Bbar[b,t,c,n] * xc[b,t,c]
         y[b, t, c]  = sum_n Cn[b,t,n] * h[b, c, n] + D[c] * xc[b,t,c]
+    where Bbar = delta * Bn (the pages' approximation, the default) or, with ``zoh``, the exact zero-order
+    hold of the same section's discretisation equation, (delta A)^-1 (exp(delta A) - 1) delta Bn, which for
+    the diagonal A is expm1(delta * A) / A * Bn.
     Returns (y [B, L, C], h after the last token [B, C, N]).
     """
     B, L, C = xc.shape
@@ -118,7 +122,11 @@ def selective_scan(xc: np.ndarray, delta: np.ndarray, A_log: np.ndarray, Bn: np.
     for t in range(L):
         dt = delta[:, t, :]                                    # [B, C]
         abar = np.exp(dt[:, :, None] * A[None, :, :])          # [B, C, N]
-        bbar_x = (dt * xc[:, t, :])[:, :, None] * Bn[:, t, None, :]
+        if zoh:
+            bbar = np.expm1(dt[:, :, None] * A[None, :, :]) / A[None, :, :] * Bn[:, t, None, :]
+            bbar_x = bbar * xc[:, t, :, None]
+        else:
+            bbar_x = (dt * xc[:, t, :])[:, :, None] * Bn[:, t, None, :]
         h = abar * h + bbar_x
         y[:, t, :] = np.sum(h * Cn[:, t, None, :], axis=-1) + D * xc[:, t, :]
     return y, h
@@ -127,14 +135,15 @@ def selective_scan(xc: np.ndarray, delta: np.ndarray, A_log: np.ndarray, Bn: np.
 def mixer_prefill(x: np.ndarray, z: np.ndarray, w: Dict[str, np.ndarray], dt_rank: int, d_state: int,
                   eps: float = 1e-6, conv_state: Optional[np.ndarray] = None,
                   ssm_state: Optional[np.ndarray] = None, channels: Optional[Sequence[int]] = None,
-                  return_intermediates: bool = False):
+                  return_intermediates: bool = False, zoh: bool = False):
     """The mixer from x, z to the gated output, plus the final conv and SSM states.
 
     ``w`` holds conv_w, conv_b, x_proj_w, dt_norm_w, b_norm_w, c_norm_w, dt_proj_w, dt_proj_b, A_log, D.
     With ``channels`` given, steps 4-7 (dt_proj, scan, gate) are evaluated for those channels only; steps
     1-3 always cover every channel because x_proj contracts over all of them.  ``ssm_state`` then holds the
     selected channels only ([B, len(channels), N]), and so does the returned SSM state; the conv state is
-    always full.  Returns (out, conv_state_out, ssm_state_out[, intermediates]).
+    always full.  ``zoh`` selects the exact zero-order-hold input matrix in the scan (see selective_scan).
+    Returns (out, conv_state_out, ssm_state_out[, intermediates]).
     """
     xc, conv_out = causal_conv1d_silu(x, w["conv_w"], w.get("conv_b"), conv_state)
     dbc = x_proj(xc, w["x_proj_w"])
@@ -144,7 +153,7 @@ def mixer_prefill(x: np.ndarray, z: np.ndarray, w: Dict[str, np.ndarray], dt_ran
     cn = rms_norm(cv, w["c_norm_w"], eps)
     sel = slice(None) if channels is None else np.asarray(channels)
     delta = dt_proj_softplus(dln, w["dt_proj_w"][sel], w["dt_proj_b"][sel])
-    y, h = selective_scan(xc[..., sel], delta, w["A_log"][sel], bn, cn, w["D"][sel], ssm_state)
+    y, h = selective_scan(xc[..., sel], delta, w["A_log"][sel], bn, cn, w["D"][sel], ssm_state, zoh)
     out = y * silu(z[..., sel])
     if not return_intermediates:
         return out, conv_out, h
@@ -153,10 +162,10 @@ def mixer_prefill(x: np.ndarray, z: np.ndarray, w: Dict[str, np.ndarray], dt_ran
 
 
 def mixer_decode_step(x_t: np.ndarray, z_t: np.ndarray, w: Dict[str, np.ndarray], dt_rank: int, d_state: int,
-                      conv_state: np.ndarray, ssm_state: np.ndarray, eps: float = 1e-6):
+                      conv_state: np.ndarray, ssm_state: np.ndarray, eps: float = 1e-6, zoh: bool = False):
     """One decode step: the prefill definition with L = 1.  x_t, z_t are [B, C]."""
     out, conv_out, h = mixer_prefill(x_t[:, None, :], z_t[:, None, :], w, dt_rank, d_state, eps,
-                                     conv_state, ssm_state)
+                                     conv_state, ssm_state, zoh=zoh)
     return out[:, 0, :], conv_out, h
 
 

@@ -57,8 +57,9 @@ def _rows(nseq: int, slots: Optional[Sequence[int]]) -> List[int]:
 
 def mixer_prefill_varlen(x: np.ndarray, z: np.ndarray, cu_seqlens: Sequence[int], w: Dict[str, np.ndarray],
                          dt_rank: int, d_state: int, eps: float = 1e-6, conv_state: Optional[np.ndarray] = None,
-                         ssm_state: Optional[np.ndarray] = None, slots: Optional[Sequence[int]] = None):
-    """The mixer over a packed batch.
+                         ssm_state: Optional[np.ndarray] = None, slots: Optional[Sequence[int]] = None,
+                         zoh: bool = False):
+    """The mixer over a packed batch (``zoh``: the exact zero-order-hold input matrix, see oracle.mixer).
 
     x, z [T, C] hold the sequences back to back; sequence s is rows [cu[s], cu[s+1]).  The state tensors
     conv_state [R, C, K-1] / ssm_state [R, C, N] (None: zeros) give sequence s the initial states of row s,
@@ -82,7 +83,7 @@ def mixer_prefill_varlen(x: np.ndarray, z: np.ndarray, cu_seqlens: Sequence[int]
         h0 = gather_rows(ssm_state, [rows[s]], (C, d_state))
         if cu[s + 1] > cu[s]:
             o, cf, hf = mixer_prefill(x[None, cu[s]:cu[s + 1]], z[None, cu[s]:cu[s + 1]], w, dt_rank, d_state, eps,
-                                      c0, h0)
+                                      c0, h0, zoh=zoh)
             out[cu[s]:cu[s + 1]] = o[0]
         else:
             cf, hf = c0, h0
