@@ -46,7 +46,7 @@
  *      ordered dt | B | C, dt_norm_w [R], b_norm_w [N], c_norm_w [N], dt_proj_w [C, R], dt_proj_b [C],
  *      A_log [C, N], D [C] — all contiguous, in io_dtype.
  *  - Requirements (else an error is returned and nothing is enqueued or written):
- *      d_state == 16, d_conv == 4, d_inner a positive multiple of 64, 1 <= dt_rank <= 512 with
+ *      discretization a jm_discretization value, d_state == 16, d_conv == 4, d_inner a positive multiple of 64, 1 <= dt_rank <= 512 with
  *      dt_rank % 8 == 0, batch >= 1, 0 <= seqlen <= 2097152 (2^21) for a prefill, row strides >= d_inner
  *      and multiples of 8 elements, every pointer 16-byte aligned (int32 index vectors: 4-byte), and
  *      norm_eps >= 0.
@@ -75,6 +75,14 @@ enum jm_status {
 
 enum jm_dtype { JM_F32 = 0, JM_BF16 = 1 };
 
+/*
+ * The input matrix of the discretised recurrence.  The Jamba Guide's discretisation equation gives the exact
+ * zero-order hold (dt A)^-1 (exp(dt A) - I) dt B and, as its approximation, dt B:
+ *   JM_DISC_EULER  Bbar = dt * B                        (the default; what the rest of this header describes)
+ *   JM_DISC_ZOH    Bbar = (exp(dt * A) - 1) / A * B     (A diagonal; for |dt A| < 1/16 evaluated by its series)
+ */
+enum jm_discretization { JM_DISC_EULER = 0, JM_DISC_ZOH = 1 };
+
 /* Sizes of one call.  For jm_mixer_decode_step, seqlen is ignored (one token per sequence). */
 typedef struct jm_mixer_dims {
   int32_t batch;
@@ -87,6 +95,8 @@ typedef struct jm_mixer_dims {
   float norm_eps;        /* epsilon of the three RMSNorms (1e-6 for Jamba) */
   int64_t x_row_stride;  /* elements between consecutive tokens of x; 0 means d_inner */
   int64_t z_row_stride;  /* elements between consecutive tokens of z; 0 means d_inner */
+  int32_t discretization; /* enum jm_discretization (0: dt * B) */
+  int32_t reserved;       /* must be 0 */
 } jm_mixer_dims;
 
 /* Device pointers to the mixer's weights, all in io_dtype.  conv_b may be NULL (zero bias). */

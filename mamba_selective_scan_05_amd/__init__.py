@@ -6,7 +6,7 @@ SiLU(z) gate) as hand-written HIP kernels for AMD MI355X (gfx950), behind the C 
 residual).
 """
 
-from ._lib import (JM_BF16, JM_F32, JMError, Mixer, Dims, Weights, WorkspaceLayout, call_decode_step,  # noqa: F401
+from ._lib import (JM_BF16, JM_DISC_EULER, JM_DISC_ZOH, JM_F32, JMError, Mixer, Dims, Weights, WorkspaceLayout, call_decode_step,  # noqa: F401
                    call_prefill, decode_workspace_size, lib, make_dims, pack_weights, prefill_workspace_size,
                    status_string, workspace_layout)
 from ._lib import Layer, LayerDims, LayerWeights, call_layer, layer_workspace_size, make_layer_dims  # noqa: F401

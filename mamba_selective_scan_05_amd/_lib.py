@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libjm_mixer.so")
 
 JM_OK, JM_ERR_INVALID_ARG, JM_ERR_UNSUPPORTED, JM_ERR_ALIGNMENT, JM_ERR_WORKSPACE, JM_ERR_HIP = 0, -1, -2, -3, -4, -5
 JM_F32, JM_BF16 = 0, 1
+JM_DISC_EULER, JM_DISC_ZOH = 0, 1
 
 WEIGHT_NAMES = ("conv_w", "conv_b", "x_proj_w", "dt_norm_w", "b_norm_w", "c_norm_w", "dt_proj_w", "dt_proj_b",
                 "A_log", "D")
@@ -35,7 +36,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("d_inner", ctypes.c_int32),
                 ("d_state", ctypes.c_int32), ("dt_rank", ctypes.c_int32), ("d_conv", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
-                ("x_row_stride", ctypes.c_int64), ("z_row_stride", ctypes.c_int64)]
+                ("x_row_stride", ctypes.c_int64), ("z_row_stride", ctypes.c_int64),
+                ("discretization", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -134,8 +136,11 @@ def status_string(status: int) -> str:
 
 
 def make_dims(batch: int, seqlen: int, d_inner: int, dt_rank: int, io_dtype: int, d_state: int = 16,
-              d_conv: int = 4, norm_eps: float = 1e-6, x_row_stride: int = 0, z_row_stride: int = 0) -> Dims:
-    return Dims(batch, seqlen, d_inner, d_state, dt_rank, d_conv, io_dtype, norm_eps, x_row_stride, z_row_stride)
+              d_conv: int = 4, norm_eps: float = 1e-6, x_row_stride: int = 0, z_row_stride: int = 0,
+              discretization: int = 0) -> Dims:
+    """discretization: JM_DISC_EULER (0, dt * B) or JM_DISC_ZOH (1, the exact zero-order hold)."""
+    return Dims(batch, seqlen, d_inner, d_state, dt_rank, d_conv, io_dtype, norm_eps, x_row_stride, z_row_stride,
+                discretization, 0)
 
 
 def prefill_workspace_size(dims: Dims) -> int:
@@ -248,7 +253,8 @@ class Mixer:
     """Holds the weights (device tensors in the I/O dtype) and a reusable workspace."""
 
     def __init__(self, weights: Dict[str, torch.Tensor], dt_rank: int, d_state: int = 16, d_conv: int = 4,
-                 norm_eps: float = 1e-6):
+                 norm_eps: float = 1e-6, zoh: bool = False):
+        self.zoh = zoh
         self.w = {k: v.contiguous() for k, v in weights.items()}
         self.packed = pack_weights(self.w)
         self.dt_rank, self.d_state, self.d_conv, self.eps = dt_rank, d_state, d_conv, norm_eps
@@ -259,7 +265,7 @@ class Mixer:
 
     def dims(self, batch: int, seqlen: int, x_row_stride: int = 0, z_row_stride: int = 0) -> Dims:
         return make_dims(batch, seqlen, self.d_inner, self.dt_rank, _io_dtype(self.w["conv_w"]), self.d_state,
-                         self.d_conv, self.eps, x_row_stride, z_row_stride)
+                         self.d_conv, self.eps, x_row_stride, z_row_stride, JM_DISC_ZOH if self.zoh else JM_DISC_EULER)
 
     def workspace(self, nbytes: int) -> torch.Tensor:
         if self._ws is None or self._ws.numel() < nbytes:
@@ -381,9 +387,9 @@ class Mixer:
 
 def make_layer_dims(batch: int, seqlen: int, d_inner: int, dt_rank: int, io_dtype: int, d_model: int,
                     d_state: int = 16, d_conv: int = 4, norm_eps: float = 1e-6,
-                    layer_norm_eps: float = 1e-6) -> LayerDims:
-    return LayerDims(make_dims(batch, seqlen, d_inner, dt_rank, io_dtype, d_state, d_conv, norm_eps), d_model,
-                     layer_norm_eps)
+                    layer_norm_eps: float = 1e-6, discretization: int = 0) -> LayerDims:
+    return LayerDims(make_dims(batch, seqlen, d_inner, dt_rank, io_dtype, d_state, d_conv, norm_eps,
+                               discretization=discretization), d_model, layer_norm_eps)
 
 
 def layer_workspace_size(dims: LayerDims, decode: bool = False) -> int:
@@ -403,8 +409,9 @@ class Layer:
     weights (device tensors in the I/O dtype) and a reusable workspace."""
 
     def __init__(self, layer_weights: Dict[str, torch.Tensor], mixer_weights: Dict[str, torch.Tensor], dt_rank: int,
-                 d_state: int = 16, d_conv: int = 4, norm_eps: float = 1e-6, layer_norm_eps: float = 1e-6):
-        self.mixer = Mixer(mixer_weights, dt_rank, d_state, d_conv, norm_eps)
+                 d_state: int = 16, d_conv: int = 4, norm_eps: float = 1e-6, layer_norm_eps: float = 1e-6,
+                 zoh: bool = False):
+        self.mixer = Mixer(mixer_weights, dt_rank, d_state, d_conv, norm_eps, zoh)
         self.lw = {k: v.contiguous() for k, v in layer_weights.items()}
         self.packed = LayerWeights(*[_ptr(self.lw[n]) for n in LAYER_WEIGHT_NAMES], self.mixer.packed)
         self.d_model = self.lw["norm_w"].shape[0]
@@ -415,7 +422,7 @@ class Layer:
     def dims(self, batch: int, seqlen: int) -> LayerDims:
         m = self.mixer
         return make_layer_dims(batch, seqlen, m.d_inner, m.dt_rank, _io_dtype(m.w["conv_w"]), self.d_model,
-                               m.d_state, m.d_conv, m.eps, self.layer_eps)
+                               m.d_state, m.d_conv, m.eps, self.layer_eps, JM_DISC_ZOH if m.zoh else JM_DISC_EULER)
 
     def workspace(self, nbytes: int) -> torch.Tensor:
         if self._ws is None or self._ws.numel() < nbytes:

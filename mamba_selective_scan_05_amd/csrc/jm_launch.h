@@ -86,6 +86,8 @@ struct ScanArgs {
   const int32_t* cu;
   int nseq;
   float* snap;
+  // 1: the input matrix is the exact zero-order hold (exp(dt A) - 1) / A * B instead of dt * B
+  int zoh;
 };
 
 // The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.

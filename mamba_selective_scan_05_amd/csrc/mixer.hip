@@ -55,6 +55,8 @@ int check_dims(const jm_mixer_dims* d, bool decode) {
   if (!(d->norm_eps >= 0.0f)) return JM_ERR_INVALID_ARG;
   if (d->io_dtype != JM_F32 && d->io_dtype != JM_BF16) return JM_ERR_UNSUPPORTED;
   if (d->d_state != kN || d->d_conv != kTaps) return JM_ERR_UNSUPPORTED;
+  if (d->discretization != JM_DISC_EULER && d->discretization != JM_DISC_ZOH) return JM_ERR_UNSUPPORTED;
+  if (d->reserved != 0) return JM_ERR_INVALID_ARG;
   if (d->d_inner % 64 != 0) return JM_ERR_UNSUPPORTED;
   if (d->dt_rank > kMaxR || d->dt_rank % 8 != 0) return JM_ERR_UNSUPPORTED;
   const int64_t xs = d->x_row_stride ? d->x_row_stride : d->d_inner;
@@ -253,6 +255,7 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.cu = ex.cu;
   a.nseq = p.nseq;
   a.snap = p.off_snap >= 0 ? (float*)(base + p.off_snap) : nullptr;
+  a.zoh = dims->discretization == JM_DISC_ZOH;
   // the scan records events[4] (local pass), events[5] (carry pass) and events[6] (full pass)
   jm::launch_scan(p.bf16, a, st, events ? &marks.ev[4] : nullptr);
   marks.mark(JM_STAGES);

@@ -112,7 +112,17 @@ __device__ __forceinline__ void state_store(float* dst, float* hs, int lane, con
 // sequence; at a sequence start the state is reset to that sequence's initial state, and the local pass
 // marks the piece as reset (its end state then no longer depends on the incoming state).  The full pass
 // stores a sequence's final state where it ends.
-template <typename T, bool FULL, bool VAR>
+// The exact zero-order-hold input coefficient (exp(dt A) - 1) / A (the discretisation equation's first form,
+// (dt A)^-1 (exp(dt A) - 1) dt, for a diagonal A), given e = exp(dt A) and 1 / A.  For |dt A| < 1/16, where
+// e - 1 would lose digits, it is the series dt (1 + z/2 + z^2/6 + z^3/24), z = dt A (truncation < 2e-7).
+__device__ __forceinline__ float zoh_coef(float dt, float e, float A, float iA) {
+  const float z = dt * A;
+  const float series = dt * fmaf(z, fmaf(z, fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+  return fabsf(z) < 0.0625f ? series : (e - 1.0f) * iA;
+}
+
+// ZOH: the input matrix is the exact zero-order hold instead of dt * B (a variant of the same recurrence).
+template <typename T, bool FULL, bool VAR, bool ZOH = false>
 __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   const int c = blockIdx.x * 64 + threadIdx.x;
   const int p = blockIdx.y;
@@ -123,6 +133,14 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float hs[64 * kN];
   float a2[kN], h[kN];
   load_a2((const T*)a.A_log, c, a2);
+  float Av[ZOH ? kN : 1], iA[ZOH ? kN : 1];
+  if (ZOH) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      Av[n] = -exp2_fast(io<T>::ld((const T*)a.A_log + (int64_t)c * kN + n) * kLog2e);
+      iA[n] = 1.0f / Av[n];
+    }
+  }
   // the SSM state row of sequence b (VAR: of the sequence holding the piece's first token): b itself, or
   // its slot in a state pool (-1: none)
   int s = 0;
@@ -214,18 +232,23 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     const float dt = Raw<T>::f(draw);
     const float xv = Raw<T>::f(xraw);
     const float u = dt * xv;
+    // the input term of state n: dt * x * B_n, or with ZOH (exp(dt A_n) - 1) / A_n * x * B_n
+    auto input = [&](int n) __attribute__((always_inline)) {
+      if (ZOH) return zoh_coef(dt, e[n], Av[ZOH ? n : 0], iA[ZOH ? n : 0]) * (xv * Bt[n]);
+      return u * Bt[n];
+    };
     if (FULL) {
       float y = 0.0f;
 #pragma unroll
       for (int n = 0; n < kN; ++n) {
-        h[n] = fmaf(e[n], h[n], u * Bt[n]);
+        h[n] = fmaf(e[n], h[n], input(n));
         y = fmaf(Ct[n], h[n], y);
       }
       y = fmaf(Dc, xv, y);
       Raw<T>::st(ores, voff, (uint32_t)i * row_bytes, y * g);
     } else {
 #pragma unroll
-      for (int n = 0; n < kN; ++n) h[n] = fmaf(e[n], h[n], u * Bt[n]);
+      for (int n = 0; n < kN; ++n) h[n] = fmaf(e[n], h[n], input(n));
       sdt += dt;
     }
   };
@@ -417,7 +440,7 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
   }
 }
 
-template <typename T, bool VAR>
+template <typename T, bool VAR, bool ZOH>
 void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   auto mark = [&](int i) {
     if (marks) (void)hipEventRecord((hipEvent_t)marks[i], st);
@@ -425,7 +448,7 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   mark(0);
   if (a.P > 1) {
     dim3 gl(a.C / 64, a.P - 1, a.B);
-    hipLaunchKernelGGL((scan_pass_kernel<T, false, VAR>), gl, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((scan_pass_kernel<T, false, VAR, ZOH>), gl, dim3(64), 0, st, a);
   }
   mark(1);
   if (a.P > 1) {
@@ -435,7 +458,18 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   }
   mark(2);
   dim3 gf(a.C / 64, a.P, a.B);
-  hipLaunchKernelGGL((scan_pass_kernel<T, true, VAR>), gf, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((scan_pass_kernel<T, true, VAR, ZOH>), gf, dim3(64), 0, st, a);
+}
+
+template <typename T>
+void run_scan_t(const ScanArgs& a, hipStream_t st, void* const* marks) {
+  if (a.cu) {
+    if (a.zoh) run_scan<T, true, true>(a, st, marks);
+    else run_scan<T, true, false>(a, st, marks);
+  } else {
+    if (a.zoh) run_scan<T, false, true>(a, st, marks);
+    else run_scan<T, false, false>(a, st, marks);
+  }
 }
 
 }  // namespace
@@ -456,13 +490,8 @@ void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st) {
 }
 
 void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks) {
-  if (a.cu) {
-    if (bf16) run_scan<bf16_t, true>(a, st, marks);
-    else run_scan<float, true>(a, st, marks);
-  } else {
-    if (bf16) run_scan<bf16_t, false>(a, st, marks);
-    else run_scan<float, false>(a, st, marks);
-  }
+  if (bf16) run_scan_t<bf16_t>(a, st, marks);
+  else run_scan_t<float>(a, st, marks);
 }
 
 }  // namespace jm

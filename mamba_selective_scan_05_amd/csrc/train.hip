@@ -112,6 +112,7 @@ jm::ScanArgs scan_args(const jm_scan_dims* d, const void* x, const void* delta, 
   a.cu = nullptr;
   a.nseq = 0;
   a.snap = nullptr;
+  a.zoh = 0;
   return a;
 }
 

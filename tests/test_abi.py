@@ -226,3 +226,12 @@ def test_scan_train_validation_before_launch():
     e = jm.scan_dims(2, 0, 128, jm.JM_BF16)
     assert L.jm_scan_backward(ctypes.byref(e), None, None, None, None, FAKE, FAKE, None, None, None, None, None,
                               None, None, FAKE, FAKE, None, FAKE, 0, None) == _lib.JM_ERR_WORKSPACE
+
+
+def test_discretization_field():
+    assert _call(_dims(discretization=2)) == _lib.JM_ERR_UNSUPPORTED
+    d = _dims(discretization=jm.JM_DISC_ZOH)
+    assert _call(d, ws_bytes=16) == _lib.JM_ERR_WORKSPACE          # the variant is accepted
+    d.reserved = 1
+    assert _call(d) == _lib.JM_ERR_INVALID_ARG
+    assert ctypes.sizeof(jm.Dims) == 56
