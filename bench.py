@@ -154,14 +154,14 @@ def stage_groups(stage_ms):
     }
 
 
-def time_prefill(jm, cfg, steps, warmup, hip):
+def time_prefill(jm, cfg, steps, warmup, hip, zoh=False):
     import torch
     from jm_inputs import make_activations, make_weights
 
     dev = "cuda"
     w = make_weights(cfg, dev)
     a = make_activations(cfg, dev)
-    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps, zoh=zoh)
     B, L, C = cfg.batch, cfg.seqlen, cfg.d_inner
     out = torch.empty((B, L, C), dtype=cfg.torch_dtype, device=dev)
     cs = torch.empty((B, C, cfg.d_conv - 1), dtype=cfg.torch_dtype, device=dev)
@@ -535,6 +535,7 @@ def main():
     ap.add_argument("--config", type=int, default=1, choices=(1, 2, 3),
                     help="prefill workload: 1 = B1 L4096 (default), 2 = B8 L4096, 3 = B1 L262144")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
+    ap.add_argument("--no-variants", action="store_true", help="skip the ZOH-variant prefill timing")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the gated scan's training forward / backward timing")
     ap.add_argument("--training-only", action="store_true",
@@ -657,6 +658,15 @@ def main():
         if "decode" in result:
             result["serving"]["decode_slots"]["vs_plain_decode"] = round(
                 result["decode"]["us_per_step"] / result["serving"]["decode_slots"]["us_per_step"], 3)
+    if not args.no_variants and args.config == 1:
+        # the exact zero-order-hold input matrix instead of dt * B, same workload
+        log(f"prefill {cfg.name} with the exact ZOH input matrix: warmup {args.warmup}, steps {args.steps}")
+        zp = time_prefill(jm, cfg, args.steps, args.warmup, hip, zoh=True)
+        zg = stage_groups(zp["stage_ms"])
+        result["variants"] = {"zoh_prefill": {
+            "workload": f"{cfg.name} with the exact zero-order-hold input matrix (exp(dt A) - 1) / A * B",
+            "us_per_step": round(zp["ms"] * 1e3, 2), "tokens_per_s": round(tokens / (zp["ms"] * 1e-3), 1),
+            "scan_gate_us": round(zg["scan_gate"] * 1e3, 2), "vs_default": round(pre["ms"] / zp["ms"], 3)}}
     if not args.no_training and args.config == 1:
         log(f"training (scan forward / backward): warmup {args.warmup}, steps {args.steps}")
         result["training"] = time_training(jm, args.steps, args.warmup)
