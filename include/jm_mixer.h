@@ -47,7 +47,7 @@
  *      A_log [C, N], D [C] — all contiguous, in io_dtype.
  *  - Requirements (else an error is returned and nothing is enqueued or written):
  *      discretization a jm_discretization value, d_state == 16, d_conv == 4, d_inner a positive multiple of 64, 1 <= dt_rank <= 512 with
- *      dt_rank % 8 == 0, batch >= 1, 0 <= seqlen <= 2097152 (2^21) for a prefill, row strides >= d_inner
+ *      dt_rank % 8 == 0, 1 <= batch <= 65536, 0 <= seqlen <= 2097152 (2^21) for a prefill, row strides >= d_inner
  *      and multiples of 8 elements, every pointer 16-byte aligned (int32 index vectors: 4-byte), and
  *      norm_eps >= 0.
  *  - Errors: every entry point returns JM_OK (0) or a negative jm_status.  Arguments are validated on

@@ -19,7 +19,7 @@
  *   x (the scan input, the conv output xc), delta, z, out, dout and their gradients: [batch, seqlen, C] in
  *   io_dtype;  bc and dbc: [T, 2N] float32, B_t in columns 0..N-1 and C_t in N..2N-1 (shared by all
  *   channels);  A_log [C, N] and D [C] in io_dtype, their gradients float32;  states [batch, C, N] float32.
- * Requirements: d_state == 16, d_inner a positive multiple of 64, batch >= 1, 0 <= seqlen <= 2^21, every
+ * Requirements: d_state == 16, d_inner a positive multiple of 64, 1 <= batch <= 65536, 0 <= seqlen <= 2^21, every
  * pointer 16-byte aligned.
  */
 #ifndef JM_SCAN_H

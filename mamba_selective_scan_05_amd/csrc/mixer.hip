@@ -12,7 +12,8 @@ constexpr int kN = 16;       // d_state the kernels are built for
 constexpr int kTaps = 4;     // d_conv the kernels are built for
 constexpr int kMaxR = 512;   // dt_rank bound of the norm kernel
 constexpr int64_t kAlign = 256;
-constexpr int kMaxSeqlen = 1 << 21;   // tokens of a prefill call (the conv's grid rows stay under 65536)
+constexpr int kMaxSeqlen = 1 << 21;   // tokens of a prefill call (the conv's grid rows stay within 65536)
+constexpr int kMaxBatch = 1 << 16;    // sequences of a call (they index the grid's y / z axes, at most 65536)
 
 // Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.
 #ifndef JM_SCAN_WAVE_TARGET
@@ -50,6 +51,7 @@ int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int check_dims(const jm_mixer_dims* d, bool decode) {
   if (!d) return JM_ERR_INVALID_ARG;
   if (d->batch < 1 || d->d_inner < 1 || d->dt_rank < 1) return JM_ERR_INVALID_ARG;
+  if (d->batch > kMaxBatch) return JM_ERR_UNSUPPORTED;
   if (!decode && d->seqlen < 0) return JM_ERR_INVALID_ARG;
   if (!decode && d->seqlen > kMaxSeqlen) return JM_ERR_UNSUPPORTED;
   if (!(d->norm_eps >= 0.0f)) return JM_ERR_INVALID_ARG;

@@ -455,8 +455,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dtproj_mfma_stream_kernel(const bf
 __global__ __launch_bounds__(256) void dtproj_f32_kernel(const float* __restrict__ dln, const float* __restrict__ w,
                                                          const float* __restrict__ bias, float* __restrict__ delta,
                                                          int M, int C, int R) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int m = blockIdx.y;
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  const int m = blockIdx.x;   // tokens on the grid's x axis (the y and z axes hold at most 65536 workgroups)
   if (c >= C) return;
   float acc = 0.f;
   for (int r = 0; r < R; ++r) acc = fmaf(dln[(int64_t)m * R + r], w[(int64_t)c * R + r], acc);
@@ -501,7 +501,7 @@ void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, voi
                          (const bf16_t*)b, (bf16_t*)delta, M, C, R);
     }
   } else {
-    dim3 grid((C + 255) / 256, M);
+    dim3 grid(M, (C + 255) / 256);
     hipLaunchKernelGGL(dtproj_f32_kernel, grid, dim3(256), 0, st, (const float*)dln, (const float*)w,
                        (const float*)b, (float*)delta, M, C, R);
   }

@@ -19,6 +19,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_dims(const jm_scan_dims* d) {
   if (!d) return JM_ERR_INVALID_ARG;
   if (d->batch < 1 || d->d_inner < 1 || d->seqlen < 0) return JM_ERR_INVALID_ARG;
+  if (d->batch > (1 << 16)) return JM_ERR_UNSUPPORTED;   // sequences index the grid's z axis (at most 65536)
   if (d->seqlen > kMaxSeqlen) return JM_ERR_UNSUPPORTED;
   if (d->io_dtype != JM_F32 && d->io_dtype != JM_BF16) return JM_ERR_UNSUPPORTED;
   if (d->d_state != kN || d->d_inner % 64 != 0) return JM_ERR_UNSUPPORTED;

@@ -235,3 +235,9 @@ def test_discretization_field():
     d.reserved = 1
     assert _call(d) == _lib.JM_ERR_INVALID_ARG
     assert ctypes.sizeof(jm.Dims) == 56
+
+
+def test_batch_limit():
+    assert _call(_dims(batch=(1 << 16) + 1)) == _lib.JM_ERR_UNSUPPORTED
+    assert _call(_dims(batch=1 << 16), ws_bytes=16) == _lib.JM_ERR_WORKSPACE
+    assert jm.scan_workspace_size(jm.scan_dims((1 << 16) + 1, 64, 128, jm.JM_BF16)) == 0
