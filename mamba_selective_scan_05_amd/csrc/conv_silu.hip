@@ -294,14 +294,9 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x,
   // thread's 16 bytes of input
   uint4 rs[S3], rx;
   // the state row of sequence b: b itself, or its slot in the pool (-1: none, a zero state stored nowhere)
-  auto state_row = [&](int64_t b) -> int64_t {
-    if (!slots) return b;
-    const int s = slots[b];
-    return s >= 0 && s < pool ? s : -1;
-  };
   auto load_seq = [&](int s) {
-    const int64_t b = b0 + s;
-    const int64_t row = state_row(b);
+    const int b = b0 + s;
+    const int64_t row = state_row(slots, pool, b);
     const uint4* gst = reinterpret_cast<const uint4*>(conv_in + (max(row, (int64_t)0) * C + cbase) * S3);
 #pragma unroll
     for (int q = 0; q < S3; ++q)
@@ -342,7 +337,7 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const T* __restrict__ x,
       for (int q = 0; q < S3; ++q) store16(reinterpret_cast<T*>(&sst[tid * S3 + q]), ns + q * V);
     }
     __syncthreads();
-    const int64_t row = state_row(b);
+    const int64_t row = state_row(slots, pool, (int)b);
     if (row < 0) continue;
     uint4* gout = reinterpret_cast<uint4*>(conv_out + (row * C + cbase) * S3);
 #pragma unroll
