@@ -58,14 +58,17 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
-// sum over the four lanes of a quad (the four state groups of one channel), in every lane
+// sum over the four lanes of a quad (the four state groups of one channel), in every lane.  Contraction is
+// off so that the product feeding a sum is not folded into it: each step stays one add with a DPP source.
 __device__ __forceinline__ float quad_sum(float v) {
+#pragma clang fp contract(off)
   v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
   v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
   return v;
 }
 // sum over the four lanes of a 16-lane row holding the same state group (stride 4), in every lane
 __device__ __forceinline__ float row_q_sum(float v) {
+#pragma clang fp contract(off)
   v += dpp<0x124>(v);  // row_ror:4
   v += dpp<0x128>(v);  // row_ror:8
   return v;
@@ -294,12 +297,13 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
   };
   __syncthreads();   // sbc
 
-  // forward through the piece, saving the state at each sub-chunk start
-  {
+  // forward through the piece, saving the state at each sub-chunk start (the last sub-chunk's own tokens are
+  // not needed here)
+  ck[0][threadIdx.x] = f32x4{h[0], h[1], h[2], h[3]};
+  if (nsub > 1) {
     float dn[kSub], xn[kSub];
     load2(0, dn, xn);
-    for (int k = 0; k < nsub; ++k) {
-      ck[k][threadIdx.x] = f32x4{h[0], h[1], h[2], h[3]};
+    for (int k = 0; k + 1 < nsub; ++k) {
       float dd[kSub], xx[kSub];
 #pragma unroll
       for (int j = 0; j < kSub; ++j) {
@@ -307,16 +311,14 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
         xx[j] = xn[j];
       }
       load2(min(k + 1, nsub - 1), dn, xn);
-      const int j1 = min(kSub, n_tok - k * kSub);
 #pragma unroll
-      for (int j = 0; j < kSub; ++j) {
-        if (j < j1) {
-          const f32x4 Bv = sbc[k * kSub + j][l.q];
-          const float dx = dd[j] * xx[j];
+      for (int j = 0; j < kSub; ++j) {   // a sub-chunk before the last is always whole
+        const f32x4 Bv = sbc[k * kSub + j][l.q];
+        const float dx = dd[j] * xx[j];
 #pragma unroll
-          for (int s = 0; s < kQ; ++s) h[s] = fmaf(exp2_fast(dd[j] * a2[s]), h[s], dx * Bv[s]);
-        }
+        for (int s = 0; s < kQ; ++s) h[s] = fmaf(exp2_fast(dd[j] * a2[s]), h[s], dx * Bv[s]);
       }
+      ck[k + 1][threadIdx.x] = f32x4{h[0], h[1], h[2], h[3]};
     }
   }
 
