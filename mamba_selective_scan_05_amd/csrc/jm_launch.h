@@ -75,8 +75,8 @@ struct ScanArgs {
   float* loc;            // [B, P, N+1, C]   per-piece local end states and dt sums (P > 1)
   float* cin;            // [B, P, N, C]     per-piece incoming states (P > 1)
   int B, L, C, P, Lp;
-  // Decode with a state pool (P = 1): sequence b's SSM state is row slots[b] of h0 / h_out (pools of `pool`
-  // rows); a slot outside [0, pool) runs from a zero state and stores nothing.  Null: row b.
+  // State pools (decode, or a packed batch): sequence b's SSM state is row slots[b] of h0 / h_out (pools of
+  // `pool` rows); a slot outside [0, pool) runs from a zero state and stores nothing.  Null: row b.
   const int32_t* slots;
   int pool;
   // Packed variable-length batch (B = 1, L packed tokens): sequence s holds tokens [cu[s], cu[s+1]) and its

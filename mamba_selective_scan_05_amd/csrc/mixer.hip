@@ -1,5 +1,6 @@
 // The library's C ABI (jm_mixer.h): argument checks, the execution plan, the workspace layout, and the
-// kernel sequence on the caller's stream.  Nothing here allocates device memory.
+// kernel sequence on the caller's stream, for the plain batch, the decode step, state pools (slots) and
+// packed variable-length batches.  Nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
