@@ -451,8 +451,10 @@ def time_serving(jm, steps, warmup):
 
 
 def time_training(jm, steps, warmup):
-    """The gated scan alone at the 4K prefill's shape (B=1, L=4096, d_inner 8192, bf16): its training forward
-    (jm_scan_forward) and backward (jm_scan_backward), timed separately."""
+    """The gated scan alone at the 4K prefill's shape (B=1, L=4096, d_inner 8192, bf16): its forward
+    (jm_scan_forward) and backward (jm_scan_backward, recomputing the piece states), timed separately, and
+    the training pair that passes the states from one to the other (jm_scan_forward_train, then
+    jm_scan_backward given the saved states)."""
     import torch
     from jm_inputs import CONFIGS, make_scan_problem
 
@@ -470,6 +472,7 @@ def time_training(jm, steps, warmup):
     dA = torch.empty((C, N), dtype=torch.float32, device="cuda")
     dD = torch.empty((C,), dtype=torch.float32, device="cuda")
     dh0 = torch.empty((B, C, N), dtype=torch.float32, device="cuda")
+    saved = torch.empty(jm.scan_saved_states_size(dims) // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
 
@@ -480,16 +483,28 @@ def time_training(jm, steps, warmup):
         if s != 0:
             raise jm.JMError(s, "jm_scan_forward")
 
-    def bwd(i):
+    def fwd_train(i):
+        s = L_.jm_scan_forward_train(ctypes.byref(dims), ptr(p["x"]), ptr(p["delta"]), ptr(p["z"]), ptr(p["bc"]),
+                                     ptr(p["A_log"]), ptr(p["D"]), ptr(p["h0"]), ptr(out), ptr(h_out), ptr(saved),
+                                     ptr(wsf), wsf.numel(), stream)
+        if s != 0:
+            raise jm.JMError(s, "jm_scan_forward_train")
+
+    def bwd(i, states=None):
         s = L_.jm_scan_backward(ctypes.byref(dims), ptr(p["x"]), ptr(p["delta"]), ptr(p["z"]), ptr(p["bc"]),
                                 ptr(p["A_log"]), ptr(p["D"]), ptr(p["h0"]), ptr(p["dout"]), ptr(p["dh_final"]),
-                                ptr(g["dx"]), ptr(g["ddelta"]), ptr(g["dz"]), ptr(dbc), ptr(dA), ptr(dD), ptr(dh0),
-                                ptr(wsb), wsb.numel(), stream)
+                                ptr(states), ptr(g["dx"]), ptr(g["ddelta"]), ptr(g["dz"]), ptr(dbc), ptr(dA), ptr(dD),
+                                ptr(dh0), ptr(wsb), wsb.numel(), stream)
         if s != 0:
             raise jm.JMError(s, "jm_scan_backward")
 
+    def train_pair(i):
+        fwd_train(i)
+        bwd(i, saved)
+
     res = {"workload": f"{cfg.name}: the gated scan alone, B={B} L={L} d_inner={C}, bf16 I/O, fp32 state"}
-    for name, step in (("forward", fwd), ("backward", bwd)):
+    for name, step in (("forward", fwd), ("backward", bwd), ("forward_train", fwd_train),
+                       ("forward_train_plus_backward", train_pair)):
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -500,12 +515,15 @@ def time_training(jm, steps, warmup):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
-        ops = scan_alu_ops(B, L, C, N) if name == "forward" else scan_bwd_alu_ops(B, L, C, N)
-        ach = ops / (ms * 1e-3) / 1e12
-        res[name] = {"us": round(ms * 1e3, 2), "tokens_per_s": round(B * L / (ms * 1e-3), 1),
-                     "alg_ops": ops, "T_lane_ops_s": round(ach, 2), "frac_alu": round(ach / VALU_PEAK_TOPS, 4)}
+        res[name] = {"us": round(ms * 1e3, 2), "tokens_per_s": round(B * L / (ms * 1e-3), 1)}
+        if name in ("forward", "backward"):
+            ops = scan_alu_ops(B, L, C, N) if name == "forward" else scan_bwd_alu_ops(B, L, C, N)
+            ach = ops / (ms * 1e-3) / 1e12
+            res[name].update({"alg_ops": ops, "T_lane_ops_s": round(ach, 2),
+                              "frac_alu": round(ach / VALU_PEAK_TOPS, 4)})
         log(f"  scan {name}: {ms * 1e3:.1f} us")
     res["backward_over_forward"] = round(res["backward"]["us"] / res["forward"]["us"], 2)
+    res["saved_states_bytes"] = saved.numel() * 4
     return res
 
 

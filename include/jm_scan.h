@@ -44,6 +44,13 @@ size_t jm_scan_forward_workspace_size(const jm_scan_dims* dims);
 size_t jm_scan_backward_workspace_size(const jm_scan_dims* dims);
 
 /*
+ * Bytes of the saved states that jm_scan_forward_train writes and jm_scan_backward may read (0 if the dims are
+ * invalid): float32 [batch, ceil(seqlen / 32), C, N] laid out as [batch, piece, N, C], the state entering
+ * tokens 0, 32, 64, ... of every sequence.
+ */
+size_t jm_scan_saved_states_size(const jm_scan_dims* dims);
+
+/*
  * Forward: out [batch, seqlen, C] and the final state h_out [batch, C, N] (required) from x, delta, z, bc,
  * A_log, D and the initial state h0 (NULL: zeros).  h_out may alias h0.
  */
@@ -52,18 +59,29 @@ int jm_scan_forward(const jm_scan_dims* dims, const void* x, const void* delta, 
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same forward (out and h_out bit for bit as jm_scan_forward), that also writes saved_states (required
+ * when seqlen > 0; jm_scan_saved_states_size bytes, owned by the caller) for jm_scan_backward, which then
+ * skips recomputing them.  Workspace: jm_scan_forward_workspace_size.
+ */
+int jm_scan_forward_train(const jm_scan_dims* dims, const void* x, const void* delta, const void* z, const float* bc,
+                          const void* A_log, const void* D, const float* h0, void* out, float* h_out,
+                          float* saved_states, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward: the gradients of  sum(dout * out) + sum(dh_final * h_L)  with respect to every input.
  *   inputs   x, delta, z, bc, A_log, D, h0 (NULL: zeros) as given to the forward; dout; dh_final [batch, C, N]
  *            (the gradient arriving at the final state; NULL: zero)
  *   outputs  dx, ddelta, dz [batch, seqlen, C] in io_dtype; dbc [T, 2N] float32; dA_log [C, N] and dD [C]
  *            float32, summed over the batch; dh0 [batch, C, N] float32 (NULL: not computed)
- * The forward's states are recomputed from x, delta, bc and h0 (nothing is kept between the two calls).
+ *   saved_states  what jm_scan_forward_train wrote for these same inputs, or NULL: the backward then
+ *            recomputes the states entering its 32-token pieces from x, delta, bc and h0 itself.  Inside each
+ *            piece the states are recomputed either way.
  * Outputs must not overlap the inputs.  seqlen == 0 is valid: dA_log = dD = 0 and dh0 = dh_final.
  */
 int jm_scan_backward(const jm_scan_dims* dims, const void* x, const void* delta, const void* z, const float* bc,
                      const void* A_log, const void* D, const float* h0, const void* dout, const float* dh_final,
-                     void* dx, void* ddelta, void* dz, float* dbc, float* dA_log, float* dD, float* dh0,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     const float* saved_states, void* dx, void* ddelta, void* dz, float* dbc, float* dA_log,
+                     float* dD, float* dh0, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

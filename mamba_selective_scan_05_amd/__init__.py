@@ -11,4 +11,5 @@ from ._lib import (JM_BF16, JM_DISC_EULER, JM_DISC_ZOH, JM_F32, JMError, Mixer, 
                    status_string, workspace_layout)
 from ._lib import Layer, LayerDims, LayerWeights, call_layer, layer_workspace_size, make_layer_dims  # noqa: F401
 from ._lib import call_decode_step_slots, call_prefill_varlen, varlen_workspace_size  # noqa: F401
-from ._lib import ScanDims, scan_backward, scan_dims, scan_forward, scan_workspace_size  # noqa: F401
+from ._lib import (ScanDims, scan_backward, scan_dims, scan_forward, scan_saved_states_size,  # noqa: F401
+                   scan_workspace_size)

@@ -117,9 +117,12 @@ def lib() -> ctypes.CDLL:
         L.jm_layer_prefill_varlen_workspace_size.restype = S
         L.jm_scan_forward.argtypes = [P(ScanDims)] + [V] * 10 + [S, V]
         L.jm_scan_forward.restype = I
-        L.jm_scan_backward.argtypes = [P(ScanDims)] + [V] * 17 + [S, V]
+        L.jm_scan_forward_train.argtypes = [P(ScanDims)] + [V] * 11 + [S, V]
+        L.jm_scan_forward_train.restype = I
+        L.jm_scan_backward.argtypes = [P(ScanDims)] + [V] * 18 + [S, V]
         L.jm_scan_backward.restype = I
-        for name in ("jm_scan_forward_workspace_size", "jm_scan_backward_workspace_size"):
+        for name in ("jm_scan_forward_workspace_size", "jm_scan_backward_workspace_size",
+                     "jm_scan_saved_states_size"):
             f = getattr(L, name)
             f.argtypes = [P(ScanDims)]
             f.restype = S
@@ -542,31 +545,51 @@ def _scan_ws(dims: ScanDims, backward: bool, device) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def scan_saved_states_size(dims: ScanDims) -> int:
+    return int(lib().jm_scan_saved_states_size(ctypes.byref(dims)))
+
+
 def scan_forward(x: torch.Tensor, delta: torch.Tensor, z: torch.Tensor, bc: torch.Tensor, A_log: torch.Tensor,
-                 D: torch.Tensor, h0: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 D: torch.Tensor, h0: Optional[torch.Tensor] = None, save: bool = False):
     """The gated scan forward (jm_scan_forward): x, delta, z [B, L, C] in the I/O dtype, bc [B*L, 2N] fp32,
-    A_log [C, N], D [C]; returns (out [B, L, C], h_out [B, C, N] fp32)."""
+    A_log [C, N], D [C]; returns (out [B, L, C], h_out [B, C, N] fp32).  With save (jm_scan_forward_train),
+    also the saved states [B, ceil(L / 32), N, C] fp32 for scan_backward, as a third result."""
     B, L, C = x.shape
+    N = A_log.shape[1]
     _check_contiguous(x=x, delta=delta, z=z, bc=bc, A_log=A_log, D=D, h0=h0)
-    dims = scan_dims(B, L, C, _io_dtype(x), A_log.shape[1])
+    dims = scan_dims(B, L, C, _io_dtype(x), N)
     ws = _scan_ws(dims, False, x.device)
     out = torch.empty_like(x)
-    h_out = torch.empty((B, C, A_log.shape[1]), dtype=torch.float32, device=x.device)
-    s = lib().jm_scan_forward(ctypes.byref(dims), _ptr(x), _ptr(delta), _ptr(z), _ptr(bc), _ptr(A_log), _ptr(D),
-                              _ptr(h0), _ptr(out), _ptr(h_out), _ptr(ws), ws.numel(), _stream(x.device))
+    h_out = torch.empty((B, C, N), dtype=torch.float32, device=x.device)
+    if not save:
+        s = lib().jm_scan_forward(ctypes.byref(dims), _ptr(x), _ptr(delta), _ptr(z), _ptr(bc), _ptr(A_log),
+                                  _ptr(D), _ptr(h0), _ptr(out), _ptr(h_out), _ptr(ws), ws.numel(),
+                                  _stream(x.device))
+        if s != JM_OK:
+            raise JMError(s, "jm_scan_forward")
+        return out, h_out
+    saved = torch.empty((B, (L + 31) // 32, N, C), dtype=torch.float32, device=x.device)
+    if saved.numel() * 4 != scan_saved_states_size(dims):
+        raise JMError(JM_ERR_INVALID_ARG, "jm_scan_saved_states_size")
+    s = lib().jm_scan_forward_train(ctypes.byref(dims), _ptr(x), _ptr(delta), _ptr(z), _ptr(bc), _ptr(A_log),
+                                    _ptr(D), _ptr(h0), _ptr(out), _ptr(h_out), _ptr(saved), _ptr(ws), ws.numel(),
+                                    _stream(x.device))
     if s != JM_OK:
-        raise JMError(s, "jm_scan_forward")
-    return out, h_out
+        raise JMError(s, "jm_scan_forward_train")
+    return out, h_out, saved
 
 
 def scan_backward(x: torch.Tensor, delta: torch.Tensor, z: torch.Tensor, bc: torch.Tensor, A_log: torch.Tensor,
                   D: torch.Tensor, dout: torch.Tensor, h0: Optional[torch.Tensor] = None,
-                  dh_final: Optional[torch.Tensor] = None, need_dh0: bool = True) -> Dict[str, torch.Tensor]:
+                  dh_final: Optional[torch.Tensor] = None, need_dh0: bool = True,
+                  saved_states: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """Gradients of sum(dout * out) + sum(dh_final * h_L) (jm_scan_backward): returns dx, ddelta, dz (I/O
-    dtype), dbc [B*L, 2N], dA_log [C, N], dD [C] and dh0 [B, C, N] (fp32)."""
+    dtype), dbc [B*L, 2N], dA_log [C, N], dD [C] and dh0 [B, C, N] (fp32).  saved_states: the third result
+    of scan_forward(..., save=True) on the same inputs, or None (recomputed)."""
     B, L, C = x.shape
     N = A_log.shape[1]
-    _check_contiguous(x=x, delta=delta, z=z, bc=bc, A_log=A_log, D=D, dout=dout, h0=h0, dh_final=dh_final)
+    _check_contiguous(x=x, delta=delta, z=z, bc=bc, A_log=A_log, D=D, dout=dout, h0=h0, dh_final=dh_final,
+                      saved_states=saved_states)
     dims = scan_dims(B, L, C, _io_dtype(x), N)
     ws = _scan_ws(dims, True, x.device)
     dev = x.device
@@ -576,7 +599,8 @@ def scan_backward(x: torch.Tensor, delta: torch.Tensor, z: torch.Tensor, bc: tor
          "dD": torch.empty((C,), dtype=torch.float32, device=dev),
          "dh0": torch.empty((B, C, N), dtype=torch.float32, device=dev) if need_dh0 else None}
     s = lib().jm_scan_backward(ctypes.byref(dims), _ptr(x), _ptr(delta), _ptr(z), _ptr(bc), _ptr(A_log), _ptr(D),
-                               _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dz"]),
+                               _ptr(h0), _ptr(dout), _ptr(dh_final), _ptr(saved_states), _ptr(g["dx"]),
+                               _ptr(g["ddelta"]), _ptr(g["dz"]),
                                _ptr(g["dbc"]), _ptr(g["dA_log"]), _ptr(g["dD"]), _ptr(g["dh0"]), _ptr(ws), ws.numel(),
                                _stream(dev))
     if s != JM_OK:

@@ -88,6 +88,10 @@ struct ScanArgs {
   float* snap;
   // 1: the input matrix is the exact zero-order hold (exp(dt A) - 1) / A * B instead of dt * B
   int zoh;
+  // Training forward (plain batch, dt * B): the state entering every backward piece (tokens 0, kBwdPiece,
+  // 2 kBwdPiece, ...) -> saved [B, saved_P, N, C]; null: not saved.
+  float* saved;
+  int saved_P;
 };
 
 // The selective scan with D skip and SiLU(z) gate, split into P pieces of Lp tokens per sequence.

@@ -259,6 +259,8 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   a.nseq = p.nseq;
   a.snap = p.off_snap >= 0 ? (float*)(base + p.off_snap) : nullptr;
   a.zoh = dims->discretization == JM_DISC_ZOH;
+  a.saved = nullptr;
+  a.saved_P = 0;
   // the scan records events[4] (local pass), events[5] (carry pass) and events[6] (full pass)
   jm::launch_scan(p.bf16, a, st, events ? &marks.ev[4] : nullptr);
   marks.mark(JM_STAGES);

@@ -122,7 +122,8 @@ __device__ __forceinline__ float zoh_coef(float dt, float e, float A, float iA) 
 }
 
 // ZOH: the input matrix is the exact zero-order hold instead of dt * B (a variant of the same recurrence).
-template <typename T, bool FULL, bool VAR, bool ZOH = false>
+// SAVE (full pass of a plain batch): also write the state entering every backward piece, for the backward.
+template <typename T, bool FULL, bool VAR, bool ZOH = false, bool SAVE = false>
 __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   const int c = blockIdx.x * 64 + threadIdx.x;
   const int p = blockIdx.y;
@@ -172,6 +173,14 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
   }
   const float Dc = FULL ? io<T>::ld((const T*)a.D + c) : 0.0f;
+  // the state entering backward piece q (saved after the token before it; a boundary at this piece's start
+  // is written here, one inside it after its token, so each boundary has a single writer)
+  auto save_state = [&](int q) __attribute__((always_inline)) {
+    float* dst = a.saved + ((int64_t)b * a.saved_P + q) * kN * C + c;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) dst[(int64_t)n * C] = h[n];
+  };
+  if (SAVE && t0 % kBwdPiece == 0) save_state(t0 / kBwdPiece);
 
   // Per-piece buffer resources (the plan keeps a piece under 2 GiB), a per-lane channel offset and a
   // wave-uniform token offset.
@@ -246,6 +255,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
       }
       y = fmaf(Dc, xv, y);
       Raw<T>::st(ores, voff, (uint32_t)i * row_bytes, y * g);
+      if (SAVE && (t0 + i + 1) % kBwdPiece == 0 && i + 1 < n_tok) save_state((t0 + i + 1) / kBwdPiece);
     } else {
 #pragma unroll
       for (int n = 0; n < kN; ++n) h[n] = fmaf(e[n], h[n], input(n));
@@ -458,6 +468,12 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
   }
   mark(2);
   dim3 gf(a.C / 64, a.P, a.B);
+  if constexpr (!VAR && !ZOH) {
+    if (a.saved) {
+      hipLaunchKernelGGL((scan_pass_kernel<T, true, false, false, true>), gf, dim3(64), 0, st, a);
+      return;
+    }
+  }
   hipLaunchKernelGGL((scan_pass_kernel<T, true, VAR, ZOH>), gf, dim3(64), 0, st, a);
 }
 

@@ -114,12 +114,57 @@ jm::ScanArgs scan_args(const jm_scan_dims* d, const void* x, const void* delta, 
   a.nseq = 0;
   a.snap = nullptr;
   a.zoh = 0;
+  a.saved = nullptr;
+  a.saved_P = 0;
   return a;
+}
+
+// Backward pieces of a sequence (the saved states hold one state per piece and sequence).
+int64_t bwd_pieces(const jm_scan_dims* d) { return ((int64_t)d->seqlen + jm::kBwdPiece - 1) / jm::kBwdPiece; }
+
+int forward(const jm_scan_dims* dims, const void* x, const void* delta, const void* z, const float* bc,
+            const void* A_log, const void* D, const float* h0, void* out, float* h_out, float* saved,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  int s = check_dims(dims);
+  if (s != JM_OK) return s;
+  const bool any = dims->seqlen > 0;
+  if (!A_log || !D || !h_out || (any && (!x || !delta || !z || !bc || !out))) return JM_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, delta, z, bc, A_log, D, h0, out, h_out, saved, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return JM_ERR_ALIGNMENT;
+  const FwdPlan p = fwd_plan(dims);
+  if (!workspace || (int64_t)workspace_bytes < p.total) return JM_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (!any) {
+    copy_or_zero(h0, h_out, (int64_t)dims->batch * dims->d_inner * kN, st);
+  } else {
+    char* base = (char*)workspace;
+    jm::ScanArgs a = scan_args(dims, x, delta, z, bc, A_log, D, h0, out, h_out, p.P, p.Lp,
+                               p.off_loc >= 0 ? (float*)(base + p.off_loc) : nullptr,
+                               p.off_cin >= 0 ? (float*)(base + p.off_cin) : nullptr);
+    a.saved = saved;
+    a.saved_P = (int)bwd_pieces(dims);
+    jm::launch_scan(dims->io_dtype == JM_BF16, a, st);
+  }
+  return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t jm_scan_saved_states_size(const jm_scan_dims* dims) {
+  if (check_dims(dims) != JM_OK) return 0;
+  return (size_t)((int64_t)dims->batch * bwd_pieces(dims) * kN * dims->d_inner * 4);
+}
+
+int jm_scan_forward_train(const jm_scan_dims* dims, const void* x, const void* delta, const void* z, const float* bc,
+                          const void* A_log, const void* D, const float* h0, void* out, float* h_out,
+                          float* saved_states, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!saved_states && dims && dims->seqlen > 0) return JM_ERR_INVALID_ARG;
+  return forward(dims, x, delta, z, bc, A_log, D, h0, out, h_out, saved_states, workspace, workspace_bytes, stream);
+}
 
 size_t jm_scan_forward_workspace_size(const jm_scan_dims* dims) {
   if (check_dims(dims) != JM_OK) return 0;
@@ -134,40 +179,20 @@ size_t jm_scan_backward_workspace_size(const jm_scan_dims* dims) {
 int jm_scan_forward(const jm_scan_dims* dims, const void* x, const void* delta, const void* z, const float* bc,
                     const void* A_log, const void* D, const float* h0, void* out, float* h_out,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  int s = check_dims(dims);
-  if (s != JM_OK) return s;
-  const bool any = dims->seqlen > 0;
-  if (!A_log || !D || !h_out || (any && (!x || !delta || !z || !bc || !out))) return JM_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, delta, z, bc, A_log, D, h0, out, h_out, workspace};
-  for (const void* q : ptrs)
-    if (q && !aligned16(q)) return JM_ERR_ALIGNMENT;
-  const FwdPlan p = fwd_plan(dims);
-  if (!workspace || (int64_t)workspace_bytes < p.total) return JM_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  (void)hipGetLastError();
-  if (!any) {
-    copy_or_zero(h0, h_out, (int64_t)dims->batch * dims->d_inner * kN, st);
-  } else {
-    char* base = (char*)workspace;
-    const jm::ScanArgs a = scan_args(dims, x, delta, z, bc, A_log, D, h0, out, h_out, p.P, p.Lp,
-                                     p.off_loc >= 0 ? (float*)(base + p.off_loc) : nullptr,
-                                     p.off_cin >= 0 ? (float*)(base + p.off_cin) : nullptr);
-    jm::launch_scan(dims->io_dtype == JM_BF16, a, st);
-  }
-  return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
+  return forward(dims, x, delta, z, bc, A_log, D, h0, out, h_out, nullptr, workspace, workspace_bytes, stream);
 }
 
 int jm_scan_backward(const jm_scan_dims* dims, const void* x, const void* delta, const void* z, const float* bc,
                      const void* A_log, const void* D, const float* h0, const void* dout, const float* dh_final,
-                     void* dx, void* ddelta, void* dz, float* dbc, float* dA_log, float* dD, float* dh0,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     const float* saved_states, void* dx, void* ddelta, void* dz, float* dbc, float* dA_log,
+                     float* dD, float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
   int s = check_dims(dims);
   if (s != JM_OK) return s;
   const bool any = dims->seqlen > 0;
   if (!A_log || !D || !dA_log || !dD) return JM_ERR_INVALID_ARG;
   if (any && (!x || !delta || !z || !bc || !dout || !dx || !ddelta || !dz || !dbc)) return JM_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, delta, z, bc, A_log, D, h0, dout, dh_final, dx, ddelta, dz, dbc, dA_log, dD, dh0,
-                        workspace};
+  const void* ptrs[] = {x, delta, z, bc, A_log, D, h0, dout, dh_final, saved_states, dx, ddelta, dz, dbc, dA_log,
+                        dD, dh0, workspace};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return JM_ERR_ALIGNMENT;
   const BwdPlan p = bwd_plan(dims);
@@ -184,10 +209,13 @@ int jm_scan_backward(const jm_scan_dims* dims, const void* x, const void* delta,
   }
   char* base = (char*)workspace;
   auto at = [&](int64_t off) { return off >= 0 ? (float*)(base + off) : nullptr; };
-  // every piece's incoming state, from the forward's local and carry passes over the backward's pieces
-  const jm::ScanArgs fa = scan_args(dims, x, delta, z, bc, A_log, D, h0, dx, nullptr, p.P, jm::kBwdPiece,
-                                    at(p.off_loc), at(p.off_cin));
-  jm::launch_scan_carries(bf16, fa, st);
+  // every piece's incoming state: saved by jm_scan_forward_train, or from the forward's local and carry passes
+  // over the backward's pieces
+  if (!saved_states) {
+    const jm::ScanArgs fa = scan_args(dims, x, delta, z, bc, A_log, D, h0, dx, nullptr, p.P, jm::kBwdPiece,
+                                      at(p.off_loc), at(p.off_cin));
+    jm::launch_scan_carries(bf16, fa, st);
+  }
   jm::BwdArgs a;
   a.xc = x;
   a.delta = delta;
@@ -198,7 +226,7 @@ int jm_scan_backward(const jm_scan_dims* dims, const void* x, const void* delta,
   a.D = D;
   a.h0 = h0;
   a.dh_final = dh_final;
-  a.cin = at(p.off_cin);
+  a.cin = saved_states ? saved_states : at(p.off_cin);
   a.bloc = at(p.off_bloc);
   a.gin = at(p.off_gin);
   a.pA = at(p.off_pA);

@@ -215,17 +215,28 @@ def test_scan_train_validation_before_launch():
     assert fwd(d, x=FAKE + 4) == _lib.JM_ERR_ALIGNMENT
     assert fwd(d, ws_bytes=nf - 1) == _lib.JM_ERR_WORKSPACE
     assert fwd(jm.scan_dims(0, 64, 128, jm.JM_BF16)) == _lib.JM_ERR_INVALID_ARG
-    bwd = lambda dims, ws_bytes=WS_BIG, dx=FAKE, dA=FAKE, dout=FAKE: L.jm_scan_backward(
-        ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, dout, None, dx, FAKE, FAKE, FAKE, dA, FAKE,
-        None, FAKE, ws_bytes, None)
+    bwd = lambda dims, ws_bytes=WS_BIG, dx=FAKE, dA=FAKE, dout=FAKE, saved=None: L.jm_scan_backward(
+        ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, dout, None, saved, dx, FAKE, FAKE, FAKE, dA,
+        FAKE, None, FAKE, ws_bytes, None)
     assert bwd(d, dx=None) == _lib.JM_ERR_INVALID_ARG
     assert bwd(d, dA=None) == _lib.JM_ERR_INVALID_ARG
     assert bwd(d, dout=FAKE + 8) == _lib.JM_ERR_ALIGNMENT
+    assert bwd(d, saved=FAKE + 4) == _lib.JM_ERR_ALIGNMENT
     assert bwd(d, ws_bytes=nb - 1) == _lib.JM_ERR_WORKSPACE
     # no tokens: the activations may be NULL; only the parameter gradients are required
     e = jm.scan_dims(2, 0, 128, jm.JM_BF16)
     assert L.jm_scan_backward(ctypes.byref(e), None, None, None, None, FAKE, FAKE, None, None, None, None, None,
-                              None, None, FAKE, FAKE, None, FAKE, 0, None) == _lib.JM_ERR_WORKSPACE
+                              None, None, None, FAKE, FAKE, None, FAKE, 0, None) == _lib.JM_ERR_WORKSPACE
+    # the training forward: saved states of B * ceil(L / 32) * N * C floats, required when there are tokens
+    assert jm.scan_saved_states_size(d) == 2 * 2 * 16 * 128 * 4
+    assert jm.scan_saved_states_size(jm.scan_dims(1, 33, 64, jm.JM_F32)) == 2 * 16 * 64 * 4
+    assert jm.scan_saved_states_size(jm.scan_dims(2, 64, 96, jm.JM_BF16)) == 0
+    ftr = lambda dims, saved=FAKE, ws_bytes=WS_BIG: L.jm_scan_forward_train(
+        ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, saved, FAKE, ws_bytes, None)
+    assert ftr(d, saved=None) == _lib.JM_ERR_INVALID_ARG
+    assert ftr(d, saved=FAKE + 4) == _lib.JM_ERR_ALIGNMENT
+    assert ftr(d, ws_bytes=nf - 1) == _lib.JM_ERR_WORKSPACE
+    assert ftr(jm.scan_dims(2, 64, 96, jm.JM_BF16)) == _lib.JM_ERR_UNSUPPORTED
 
 
 def test_discretization_field():

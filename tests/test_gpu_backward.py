@@ -32,12 +32,16 @@ def _f64(t):
     return None if t is None else to_f64(t)
 
 
-def _check_backward(cfg, with_state=True):
+def _check_backward(cfg, with_state=True, saved=False):
     import mamba_selective_scan_05_amd as jm
     p = make_scan_problem(cfg, DEV, with_state)
     B, L, C, N = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state
-    log(f"[{cfg.name}] B={B} L={L} C={C} {cfg.io_dtype} state={with_state}")
-    g = jm.scan_backward(p["x"], p["delta"], p["z"], p["bc"], p["A_log"], p["D"], p["dout"], p["h0"], p["dh_final"])
+    log(f"[{cfg.name}] B={B} L={L} C={C} {cfg.io_dtype} state={with_state} saved={saved}")
+    states = None
+    if saved:
+        states = jm.scan_forward(p["x"], p["delta"], p["z"], p["bc"], p["A_log"], p["D"], p["h0"], save=True)[2]
+    g = jm.scan_backward(p["x"], p["delta"], p["z"], p["bc"], p["A_log"], p["D"], p["dout"], p["h0"], p["dh_final"],
+                         saved_states=states)
     torch.cuda.synchronize()
     bc = to_f64(p["bc"]).reshape(B, L, 2 * N)
     r = oracle.selective_scan_backward(to_f64(p["x"]), to_f64(p["delta"]), to_f64(p["A_log"]), bc[..., :N],
@@ -111,3 +115,48 @@ def test_scan_forward(io):
                                           bc[..., N:], to_f64(p["D"]), to_f64(p["z"]), to_f64(p["h0"]))
     assert_close("out", out, ro, io)
     assert_close("h_out", h, rh, io)
+
+
+def _piece_states(p, cfg):
+    """The oracle's state entering tokens 0, 32, 64, ... of every sequence: [B, ceil(L / 32), N, C]."""
+    B, L, N = cfg.batch, cfg.seqlen, cfg.d_state
+    bc = to_f64(p["bc"]).reshape(B, L, 2 * N)
+    x, dl, z, A_log, D = (to_f64(p[k]) for k in ("x", "delta", "z", "A_log", "D"))
+    h = np.zeros((B, cfg.d_inner, N)) if p["h0"] is None else to_f64(p["h0"])
+    res = []
+    for s0 in range(0, L, 32):
+        res.append(h.transpose(0, 2, 1))
+        e = min(L, s0 + 32)
+        h = oracle.scan_forward_gated(x[:, s0:e], dl[:, s0:e], A_log, bc[:, s0:e, :N], bc[:, s0:e, N:], D,
+                                      z[:, s0:e], h)[2]
+    return np.stack(res, axis=1)
+
+
+@pytest.mark.parametrize("io,L", [("f32", 700), ("bf16", 700), ("f32", 37), ("bf16", 4096)])
+def test_scan_forward_train_saves_piece_states(io, L):
+    # the training forward returns the plain forward's outputs bit for bit, plus the states at every 32-token
+    # boundary (written by whichever forward piece holds the boundary; several forward pieces at these sizes)
+    import mamba_selective_scan_05_amd as jm
+    cfg = MixerConfig(f"scan_fwd_train_{io}_{L}", batch=2, seqlen=L, d_inner=128, io_dtype=io, seed=68)
+    p = make_scan_problem(cfg, DEV)
+    log(f"[{cfg.name}] B={cfg.batch} L={L} C={cfg.d_inner} {io}")
+    args = (p["x"], p["delta"], p["z"], p["bc"], p["A_log"], p["D"], p["h0"])
+    out, h = jm.scan_forward(*args)
+    out2, h2, saved = jm.scan_forward(*args, save=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(h, h2)
+    assert saved.shape == (cfg.batch, (L + 31) // 32, cfg.d_state, cfg.d_inner)
+    assert_close("saved_states", saved, _piece_states(p, cfg), io)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_scan_backward_from_saved_states(io):
+    cfg = MixerConfig(f"scan_bwd_saved_{io}", batch=2, seqlen=300, d_inner=128, io_dtype=io, seed=61)
+    _check_backward(cfg, saved=True)
+
+
+def test_scan_backward_from_saved_states_short_and_wide():
+    _check_backward(MixerConfig("scan_bwd_saved_short", batch=3, seqlen=37, d_inner=64, io_dtype="f32", seed=62),
+                    with_state=False, saved=True)
+    _check_backward(MixerConfig("scan_bwd_saved_jamba_L1024", batch=1, seqlen=1024, d_inner=8192,
+                                io_dtype="bf16", seed=64), saved=True)
