@@ -47,13 +47,12 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 // SiLU(u) = u / (1 + e^-u).  For u -> -inf the exp overflows to inf and the reciprocal gives 0.
 __device__ __forceinline__ float silu(float u) { return u * rcp_fast(1.0f + exp2_fast(-u * kLog2e)); }
 
-// max(v, 0) as one v_max_f32.  fmaxf on a value the compiler cannot prove canonical (a matrix-core result,
-// a load) first runs it through a second v_max_f32 to quiet signalling NaNs; the inputs here carry none.
-__device__ __forceinline__ float relu(float v) {
-  float r;
-  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(v));
-  return r;
-}
+// max(v, 0) as one instruction: a signed-integer max of the bits (negative floats, -0 included, are
+// negative integers; zero and positive floats keep their order).  fmaxf on a value the compiler cannot prove
+// canonical (a matrix-core result, a load) first runs it through a second v_max_f32 to quiet signalling
+// NaNs, which the inputs here never carry.  Plain code, not inline asm: the compiler must see the read to
+// keep the wait states a matrix-core result needs before a vector instruction reads it.
+__device__ __forceinline__ float relu(float v) { return __int_as_float(max(__float_as_int(v), 0)); }
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log(1 + e^-|v|), without overflow, on the transcendental unit
 // (v_exp_f32, v_log_f32).  For v below about -17, 1 + e^v rounds to 1 and the result is 0 instead of
@@ -67,6 +66,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// The exact zero-order-hold input coefficient (exp(dt A) - 1) / A (the discretisation equation's first form,
+// (dt A)^-1 (exp(dt A) - 1) dt, for a diagonal A), given e = exp(dt A) and 1 / A.  For |dt A| < 1/16, where
+// e - 1 would lose digits, it is the series dt (1 + z/2 + z^2/6 + z^3/24), z = dt A (truncation < 2e-7).
+__device__ __forceinline__ float zoh_coef(float dt, float e, float A, float iA) {
+  const float z = dt * A;
+  const float series = dt * fmaf(z, fmaf(z, fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+  return fabsf(z) < 0.0625f ? series : (e - 1.0f) * iA;
 }
 
 // Packed variable-length batches: sequence s holds packed tokens [cu[s], cu[s+1]).  The sequence holding

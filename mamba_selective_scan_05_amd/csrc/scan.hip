@@ -112,15 +112,6 @@ __device__ __forceinline__ void state_store(float* dst, float* hs, int lane, con
 // sequence; at a sequence start the state is reset to that sequence's initial state, and the local pass
 // marks the piece as reset (its end state then no longer depends on the incoming state).  The full pass
 // stores a sequence's final state where it ends.
-// The exact zero-order-hold input coefficient (exp(dt A) - 1) / A (the discretisation equation's first form,
-// (dt A)^-1 (exp(dt A) - 1) dt, for a diagonal A), given e = exp(dt A) and 1 / A.  For |dt A| < 1/16, where
-// e - 1 would lose digits, it is the series dt (1 + z/2 + z^2/6 + z^3/24), z = dt A (truncation < 2e-7).
-__device__ __forceinline__ float zoh_coef(float dt, float e, float A, float iA) {
-  const float z = dt * A;
-  const float series = dt * fmaf(z, fmaf(z, fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
-  return fabsf(z) < 0.0625f ? series : (e - 1.0f) * iA;
-}
-
 // ZOH: the input matrix is the exact zero-order hold instead of dt * B (a variant of the same recurrence).
 // SAVE (full pass of a plain batch): also write the state entering every backward piece, for the backward.
 template <typename T, bool FULL, bool VAR, bool ZOH = false, bool SAVE = false>
