@@ -38,7 +38,8 @@ __device__ __forceinline__ void unpack16(uint4 raw, float* out) {
   for (int i = 0; i < Vec16<T>::n; ++i) out[i] = io<T>::cvt(r.v[i]);
 }
 
-constexpr int kRows = 8;   // rows per prefetch batch
+// rows per prefetch batch (B = 1, L = 4096, d_inner 8192: 29.6 us with 4, 33.1 with 8, 88 with 16)
+constexpr int kRows = 4;
 
 template <typename T>
 __device__ __forceinline__ void store16(T* p, const float* in) {
@@ -414,7 +415,7 @@ void launch_varlen_states(bool bf16, const void* x, int64_t xs, const void* conv
 void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
                       const void* conv_in, void* xc, int B, int L, int C, hipStream_t st, const VarSeqs& v) {
   const int V = bf16 ? 8 : 4;
-  const int run = 32;
+  const int run = 32;   // tokens per thread (16: 34.5 us, 64: 32.4 us with 8-row batches)
   dim3 block(256);
   dim3 grid((C / V + 255) / 256, (L + run - 1) / run, B);
   if (v.cu) {   // a packed batch: B == 1
