@@ -527,6 +527,29 @@ class Layer:
         return out
 
 
+def mixer_for(weights: Dict[str, torch.Tensor], norm_eps: float = 1e-6, zoh: bool = False) -> "Mixer":
+    """A Mixer for a weight dict, with dt_rank, d_state and d_conv read from the weight shapes."""
+    return Mixer(weights, weights["dt_proj_w"].shape[1], weights["A_log"].shape[1], weights["conv_w"].shape[-1],
+                 norm_eps, zoh)
+
+
+def prefill(x: torch.Tensor, z: torch.Tensor, weights: Dict[str, torch.Tensor],
+            conv_state: Optional[torch.Tensor] = None, ssm_state: Optional[torch.Tensor] = None,
+            norm_eps: float = 1e-6, zoh: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """jm_mixer_prefill on torch tensors: x, z [B, L, C] (row strides may exceed C), states [B, C, K-1] and
+    [B, C, N] fp32 or None (zeros); returns (out, conv_state_out, ssm_state_out).  Each call allocates its
+    workspace; a Mixer reuses one across calls."""
+    return mixer_for(weights, norm_eps, zoh).prefill(x, z, conv_state, ssm_state)
+
+
+def decode_step(x: torch.Tensor, z: torch.Tensor, weights: Dict[str, torch.Tensor], conv_state: torch.Tensor,
+                ssm_state: torch.Tensor, norm_eps: float = 1e-6, zoh: bool = False, in_place: bool = False
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """jm_mixer_decode_step on torch tensors: one token per sequence, x, z [B, C]; with in_place=True the
+    states are updated in place.  Returns (out, conv_state_out, ssm_state_out)."""
+    return mixer_for(weights, norm_eps, zoh).decode_step(x, z, conv_state, ssm_state, in_place=in_place)
+
+
 # ----------------------------------------------------------------------------- the gated scan alone (training)
 
 def scan_dims(batch: int, seqlen: int, d_inner: int, io_dtype: int, d_state: int = 16) -> ScanDims:

@@ -252,3 +252,13 @@ def test_batch_limit():
     assert _call(_dims(batch=(1 << 16) + 1)) == _lib.JM_ERR_UNSUPPORTED
     assert _call(_dims(batch=1 << 16), ws_bytes=16) == _lib.JM_ERR_WORKSPACE
     assert jm.scan_workspace_size(jm.scan_dims((1 << 16) + 1, 64, 128, jm.JM_BF16)) == 0
+
+
+def test_module_level_mixer_reads_dims_from_weight_shapes():
+    # host only: the weight dict's shapes give dt_rank, d_state and d_conv; nothing is launched
+    from jm_inputs import MixerConfig, make_weights
+    cfg = MixerConfig("shapes", batch=1, seqlen=8, d_inner=128, dt_rank=24, io_dtype="bf16", seed=5)
+    m = jm.mixer_for(make_weights(cfg), norm_eps=1e-5, zoh=True)
+    assert (m.d_inner, m.dt_rank, m.d_state, m.d_conv, m.eps, m.zoh) == (128, 24, 16, 4, 1e-5, True)
+    d = m.dims(3, 9)
+    assert (d.batch, d.seqlen, d.d_inner, d.dt_rank, d.discretization) == (3, 9, 128, 24, jm.JM_DISC_ZOH)

@@ -62,3 +62,20 @@ def test_decode_step_bitwise_equals_one_token_prefill(name, B, C, R, zoh, stride
     assert_bitwise("out in place", io, do)
     assert_bitwise("ssm_state in place", hs, dh)
     assert_bitwise("conv_state in place", cs, dc)
+
+
+def test_module_level_calls_match_the_mixer():
+    # jm.prefill / jm.decode_step (dims read from the weight shapes) are the Mixer's calls
+    import mamba_selective_scan_05_amd as jm
+    cfg = MixerConfig("module_calls", batch=2, seqlen=70, d_inner=128, dt_rank=16, io_dtype="bf16", seed=91)
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    st = make_state(cfg, DEV)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    ref = m.prefill(a["x"], a["z"], st["conv_state"], st["ssm_state"])
+    got = jm.prefill(a["x"], a["z"], w, st["conv_state"], st["ssm_state"], norm_eps=cfg.norm_eps)
+    dref = m.decode_step(a["x"][:, 0], a["z"][:, 0], st["conv_state"], st["ssm_state"])
+    dgot = jm.decode_step(a["x"][:, 0], a["z"][:, 0], w, st["conv_state"], st["ssm_state"], norm_eps=cfg.norm_eps)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("out", "conv_state", "ssm_state") * 2, got + dgot, ref + dref):
+        assert_bitwise(name, g, r)
