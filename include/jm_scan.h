@@ -45,8 +45,8 @@ size_t jm_scan_backward_workspace_size(const jm_scan_dims* dims);
 
 /*
  * Bytes of the saved states that jm_scan_forward_train writes and jm_scan_backward may read (0 if the dims are
- * invalid): float32 [batch, ceil(seqlen / 32), C, N] laid out as [batch, piece, N, C], the state entering
- * tokens 0, 32, 64, ... of every sequence.
+ * invalid): float32 [batch, ceil(seqlen / 32), N, C], entry [b, p, n, c] being state n of channel c entering
+ * token 32 p of sequence b.
  */
 size_t jm_scan_saved_states_size(const jm_scan_dims* dims);
 
