@@ -74,7 +74,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float zoh_coef(float dt, float e, float A, float iA) {
   const float z = dt * A;
   const float series = dt * fmaf(z, fmaf(z, fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
-  return fabsf(z) < 0.0625f ? series : (e - 1.0f) * iA;
+  return fabsf(z) < 0.0625f ? series : fmaf(e, iA, -iA);   // (e - 1) / A as one FMA
 }
 
 // Packed variable-length batches: sequence s holds packed tokens [cu[s], cu[s+1]).  The sequence holding
