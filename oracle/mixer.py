@@ -111,7 +111,8 @@ def selective_scan(xc: np.ndarray, delta: np.ndarray, A_log: np.ndarray, Bn: np.
         y[b, t, c]  = sum_n Cn[b,t,n] * h[b, c, n] + D[c] * xc[b,t,c]
     where Bbar = delta * Bn (the pages' approximation, the default) or, with ``zoh``, the exact zero-order
     hold of the same section's discretisation equation, (delta A)^-1 (exp(delta A) - 1) delta Bn, which for
-    the diagonal A is expm1(delta * A) / A * Bn.
+    the diagonal A is expm1(delta * A) / A * Bn; where A = 0 (A_log = -inf) that expression is 0 / 0 and
+    its value is its limit as A -> 0, delta * Bn.
     Returns (y [B, L, C], h after the last token [B, C, N]).
     """
     B, L, C = xc.shape
@@ -123,7 +124,10 @@ def selective_scan(xc: np.ndarray, delta: np.ndarray, A_log: np.ndarray, Bn: np.
         dt = delta[:, t, :]                                    # [B, C]
         abar = np.exp(dt[:, :, None] * A[None, :, :])          # [B, C, N]
         if zoh:
-            bbar = np.expm1(dt[:, :, None] * A[None, :, :]) / A[None, :, :] * Bn[:, t, None, :]
+            dA = dt[:, :, None] * A[None, :, :]
+            with np.errstate(invalid="ignore", divide="ignore"):
+                coef = np.where(A[None] == 0.0, dt[:, :, None], np.expm1(dA) / A[None, :, :])
+            bbar = coef * Bn[:, t, None, :]
             bbar_x = bbar * xc[:, t, :, None]
         else:
             bbar_x = (dt * xc[:, t, :])[:, :, None] * Bn[:, t, None, :]

@@ -76,3 +76,28 @@ def test_zoh_input_term_in_closed_form():
     A = -np.exp(A_log)
     expect = (np.exp(delta[0, 0][:, None] * A) - 1.0) / A * Bn[0, 0][None, :] * xc[0, 0][:, None]
     np.testing.assert_allclose(h[0], expect, rtol=1e-13, atol=1e-15)
+
+
+def test_zero_A_takes_the_limit_delta_B():
+    # A = 0 (A_log = -inf): (exp(delta A) - 1) / A -> delta, so ZOH and the Euler form coincide exactly and
+    # the state is h0 plus the cumulative sum of delta * B * x (no decay)
+    rng = np.random.default_rng(5)
+    B, L, C, N = 2, 11, 3, 4
+    xc = rng.normal(0, 1, (B, L, C))
+    delta = rng.uniform(0.01, 0.5, (B, L, C))
+    A_log = np.log(rng.uniform(0.5, 4.0, (C, N)))
+    A_log[1] = -np.inf                                   # channel 1 has A = 0 in every state
+    Bn, Cn = rng.normal(0, 1, (B, L, N)), rng.normal(0, 1, (B, L, N))
+    D = rng.normal(1, 0.2, C)
+    h0 = rng.normal(0, 1, (B, C, N))
+    yz, hz = _scan(xc, delta, A_log, Bn, Cn, D, h0, zoh=True)
+    ye, he = _scan(xc, delta, A_log, Bn, Cn, D, h0, zoh=False)
+    assert np.isfinite(yz).all() and np.isfinite(hz).all()
+    # equal up to the order of the products (dt * B) * x against (dt * x) * B
+    np.testing.assert_allclose(hz[:, 1], he[:, 1], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(yz[:, :, 1], ye[:, :, 1], rtol=1e-14, atol=1e-15)
+    cum = h0[:, 1][:, None] + np.cumsum((delta[:, :, 1] * xc[:, :, 1])[..., None] * Bn, axis=1)
+    np.testing.assert_allclose(hz[:, 1], cum[:, -1], rtol=1e-12, atol=1e-12)
+    # the other channels are the plain ZOH
+    _, h_rest = _scan(xc[..., [0, 2]], delta[..., [0, 2]], A_log[[0, 2]], Bn, Cn, D[[0, 2]], h0[:, [0, 2]], zoh=True)
+    np.testing.assert_array_equal(hz[:, [0, 2]], h_rest)
