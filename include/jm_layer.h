@@ -1,10 +1,12 @@
 /*
  * jm_layer.h — C ABI of the whole Jamba Mamba layer around the mixer (same library as jm_mixer.h).
  *
- * One of Jamba's Mamba layers is a pre-norm residual block around the mixer (llm-architectures-explained,
- * "Jamba v0.1", "Every architecture field": hidden size 4096, rms_norm_eps; the same page's Exported
- * PyTorch listing: an RMSNorm before each mixer; TransformerLens, "supported_architectures.jamba",
- * architecture overview: the mixer's in_proj / conv1d / x_proj / dt_proj / out_proj).  Per token:
+ * One of Jamba's Mamba layers is a pre-norm residual block around the mixer: the neurarch "Jamba" page's
+ * Structure table and Exported PyTorch listing put an RMSNorm of width 4096 (nn.RMSNorm(4096)) before each
+ * Mamba block and a residual add after it; llm-architectures-explained, "Jamba v0.1", Facts: RMSNorm, pre
+ * placement; TransformerLens, "supported_architectures.jamba", architecture overview: pre-norm, mixer,
+ * residual, and the mixer's in_proj / conv1d / x_proj / dt_proj / out_proj.  No page prints the norm's
+ * epsilon; callers pass it (Jamba's mixer norms use 1e-6).  Per token:
  *
  *   1. hn      = x_res / sqrt(mean(x_res^2) + layer_norm_eps) * norm_w      (width d_model)
  *   2. [x | z] = in_proj_w . hn               in_proj_w [2C, d_model], rows x first, then z; no bias

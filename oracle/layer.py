@@ -5,8 +5,10 @@ never calls it and shares no code with it.
 
 The layer is the mixer's pre-norm residual block, in the order the Jamba pages give its parts:
 
-  1. RMSNorm of the residual stream (width d_model)   (Jamba v0.1 architecture table: rms_norm_eps; the
-     Exported PyTorch listing: JambaRMSNorm before each mixer);
+  1. RMSNorm of the residual stream (width d_model)   (the neurarch "Jamba" page: its Structure table puts an
+     RMSNorm of normalizedShape 4096 before each Mamba block, and its Exported PyTorch listing an
+     nn.RMSNorm(4096) before each mixer; llm-architectures-explained, "Jamba v0.1", Facts: norm type RMSNorm,
+     placement pre; TransformerLens, architecture overview: pre-norm, mixer, residual);
   2. in_proj (d_model -> 2 d_inner, no bias), split into the mixer's x | z
                                                       (TransformerLens "supported_architectures.jamba",
                                                        architecture overview: in_proj ... out_proj);
@@ -16,7 +18,8 @@ The layer is the mixer's pre-norm residual block, in the order the Jamba pages g
 
 Reading taken where the pages leave it open: in_proj's rows hold x first and z second (Mamba's convention,
 the same order the library's strided x / z views assume); neither projection has a bias; the layer norm is
-the mixer's own rms_norm definition with its own weight and eps.
+the mixer's own rms_norm definition with its own weight and eps.  No page prints that eps (the listing
+leaves nn.RMSNorm at its default): the value 1e-6 of the selective-parameter norms is used.
 """
 
 from __future__ import annotations

@@ -3,7 +3,8 @@ plausible mistake (a dropped residual, the norm after in_proj or missing, x and 
 added instead of multiplied, out_proj scaling the residual) fails at least one of them.
 
 The layer: out = x_res + out_proj(mixer(in_proj(rms_norm(x_res)))) with in_proj's rows ordered x | z
-(Jamba v0.1 architecture table and Exported PyTorch listing; TransformerLens Jamba architecture overview).
+(the neurarch "Jamba" page's Structure table and Exported PyTorch listing; llm-architectures-explained,
+"Jamba v0.1", Facts; TransformerLens Jamba architecture overview).
 """
 
 import math
