@@ -25,6 +25,10 @@
  *  - The workspace holds hn, the in_proj output, y, the mixer's own workspace and hipBLASLt's; it is
  *    scratch.  The library keeps one hipBLASLt handle per device and a cache of the chosen GEMM
  *    algorithms, both created on first use (host memory, and hipBLASLt's own one-time initialisation).
+ *  - Both GEMMs (handle, descriptors, algorithm for the call's shape) are resolved during validation:
+ *    JM_ERR_HIP (hipBLASLt set-up failed) and JM_ERR_UNSUPPORTED (no algorithm for the shape) are returned
+ *    with nothing enqueued and no state written.  After that only a failed launch (JM_ERR_HIP, as for any
+ *    kernel) can end a call early, and then the states may already hold this call's update.
  */
 #ifndef JM_LAYER_H
 #define JM_LAYER_H

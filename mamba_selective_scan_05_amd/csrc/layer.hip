@@ -78,73 +78,81 @@ std::mutex g_gemm_mu;
 hipblasLtHandle_t g_handle[kMaxDevices];
 std::map<GemmKey, hipblasLtMatmulAlgo_t> g_algos;
 
-// Row-major Y[T, N] = X[T, K] . W[N, K]^T (+ R[T, N] when res is given), all of the I/O type, fp32
+// Row-major Y[T, N] = X[T, K] . W[N, K]^T (+ R[T, N] when there is a residual), all of the I/O type, fp32
 // accumulation.  In hipBLASLt's column-major terms: D[N, T] = op(A)[N, K] . B[K, T] + C with A = W (its
 // row-major [N, K] is column-major [K, N], transposed), B = X (column-major [K, T]), C = R, D = Y.
-int gemm(bool bf16, const void* X, int64_t ldx, const void* W, int64_t ldw, void* Y, int64_t ldy, const void* res,
-         int64_t ldr, int64_t T, int64_t N, int64_t K, void* ws, hipStream_t st) {
-  if (T == 0) return JM_OK;
+// A GEMM is prepared (descriptors, the device's handle, the algorithm for its shape) before the layer
+// enqueues any work, so that every failure of hipBLASLt's set-up is reported with nothing enqueued; only
+// the launch itself remains.
+struct Gemm {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr, ld = nullptr;
+  hipblasLtHandle_t handle = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+  bool residual = false;
+  Gemm() = default;
+  Gemm(const Gemm&) = delete;
+  Gemm& operator=(const Gemm&) = delete;
+  ~Gemm() {
+    if (ld) hipblasLtMatrixLayoutDestroy(ld);
+    if (lc) hipblasLtMatrixLayoutDestroy(lc);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (op) hipblasLtMatmulDescDestroy(op);
+  }
+};
+
+int gemm_prepare(Gemm* g, bool bf16, int64_t ldx, int64_t ldw, int64_t ldy, bool residual, int64_t ldr, int64_t T,
+                 int64_t N, int64_t K) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return JM_ERR_HIP;
   const hipDataType ty = bf16 ? HIP_R_16BF : HIP_R_32F;
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr, ld = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  int status = JM_ERR_HIP;
   const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
   const uint64_t wsz = kGemmWorkspace;
-  const float alpha = 1.0f, beta = res ? 1.0f : 0.0f;
-  const GemmKey key{dev, bf16 ? 1 : 0, N, T, K, ldw, ldx, res ? ldr : ldy, ldy, res != nullptr};
-  hipblasLtMatmulAlgo_t algo;
-  do {
-    if (hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) break;
-    if (hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) !=
-            HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) !=
-            HIPBLAS_STATUS_SUCCESS)
-      break;
-    if (hipblasLtMatrixLayoutCreate(&la, ty, K, N, ldw) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&lb, ty, K, T, ldx) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&lc, ty, N, T, res ? ldr : ldy) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&ld, ty, N, T, ldy) != HIPBLAS_STATUS_SUCCESS)
-      break;
-    {
-      std::lock_guard<std::mutex> lock(g_gemm_mu);
-      if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
-        g_handle[dev] = nullptr;
-        break;
-      }
-      auto it = g_algos.find(key);
-      if (it == g_algos.end()) {
-        if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS ||
-            hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz,
-                                                  sizeof(wsz)) != HIPBLAS_STATUS_SUCCESS)
-          break;
-        hipblasLtMatmulHeuristicResult_t heur[1];
-        int found = 0;
-        if (hipblasLtMatmulAlgoGetHeuristic(g_handle[dev], op, la, lb, lc, ld, pref, 1, heur, &found) !=
-                HIPBLAS_STATUS_SUCCESS ||
-            found < 1) {
-          status = JM_ERR_UNSUPPORTED;
-          break;
-        }
-        it = g_algos.emplace(key, heur[0].algo).first;
-      }
-      algo = it->second;
-    }
-    const void* C = res ? res : Y;
-    if (hipblasLtMatmul(g_handle[dev], op, &alpha, W, la, X, lb, &beta, C, lc, Y, ld, &algo, ws, wsz, st) !=
-        HIPBLAS_STATUS_SUCCESS)
-      break;
-    status = JM_OK;
-  } while (false);
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (ld) hipblasLtMatrixLayoutDestroy(ld);
-  if (lc) hipblasLtMatrixLayoutDestroy(lc);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (op) hipblasLtMatmulDescDestroy(op);
-  return status;
+  g->residual = residual;
+  if (hipblasLtMatmulDescCreate(&g->op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) return JM_ERR_HIP;
+  if (hipblasLtMatmulDescSetAttribute(g->op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) !=
+          HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatmulDescSetAttribute(g->op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) !=
+          HIPBLAS_STATUS_SUCCESS)
+    return JM_ERR_HIP;
+  if (hipblasLtMatrixLayoutCreate(&g->la, ty, K, N, ldw) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&g->lb, ty, K, T, ldx) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&g->lc, ty, N, T, residual ? ldr : ldy) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&g->ld, ty, N, T, ldy) != HIPBLAS_STATUS_SUCCESS)
+    return JM_ERR_HIP;
+  const GemmKey key{dev, bf16 ? 1 : 0, N, T, K, ldw, ldx, residual ? ldr : ldy, ldy, residual};
+  std::lock_guard<std::mutex> lock(g_gemm_mu);
+  if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
+    g_handle[dev] = nullptr;
+    return JM_ERR_HIP;
+  }
+  g->handle = g_handle[dev];
+  auto it = g_algos.find(key);
+  if (it == g_algos.end()) {
+    hipblasLtMatmulPreference_t pref = nullptr;
+    if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return JM_ERR_HIP;
+    hipblasLtMatmulHeuristicResult_t heur[1];
+    int found = 0;
+    const bool ok = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz,
+                                                          sizeof(wsz)) == HIPBLAS_STATUS_SUCCESS &&
+                    hipblasLtMatmulAlgoGetHeuristic(g->handle, g->op, g->la, g->lb, g->lc, g->ld, pref, 1, heur,
+                                                    &found) == HIPBLAS_STATUS_SUCCESS;
+    hipblasLtMatmulPreferenceDestroy(pref);
+    if (!ok || found < 1) return JM_ERR_UNSUPPORTED;
+    it = g_algos.emplace(key, heur[0].algo).first;
+  }
+  g->algo = it->second;
+  return JM_OK;
+}
+
+int gemm_launch(const Gemm& g, const void* X, const void* W, void* Y, const void* res, void* ws, hipStream_t st) {
+  const float alpha = 1.0f, beta = g.residual ? 1.0f : 0.0f;
+  const void* C = g.residual ? res : Y;
+  return hipblasLtMatmul(g.handle, g.op, &alpha, W, g.la, X, g.lb, &beta, C, g.lc, Y, g.ld, &g.algo, ws,
+                         (uint64_t)kGemmWorkspace, st) == HIPBLAS_STATUS_SUCCESS
+             ? JM_OK
+             : JM_ERR_HIP;
 }
 
 // ---------------------------------------------------------------------------------------------- the layer
@@ -211,6 +219,10 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
     return jm::mixer_run(&p.md, &lw->mixer, nullptr, nullptr, nullptr, conv_in, conv_out, h0, h_out, mws,
                          mws_bytes, stream, decode, slots, pool, cu);
   }
+  // both GEMMs resolved (handle, descriptors, algorithm) before anything is enqueued
+  Gemm in_proj, out_proj;
+  if ((s = gemm_prepare(&in_proj, bf16, p.Dm, p.Dm, 2 * p.C, false, 0, p.T, 2 * p.C, p.Dm)) != JM_OK) return s;
+  if ((s = gemm_prepare(&out_proj, bf16, p.C, p.C, p.Dm, true, p.Dm, p.T, p.Dm, p.C)) != JM_OK) return s;
   (void)hipGetLastError();
   if (bf16)
     hipLaunchKernelGGL(rms_norm_kernel<jm::bf16_t>, dim3((unsigned)p.T), dim3(256), 0, st,
@@ -220,13 +232,11 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
     hipLaunchKernelGGL(rms_norm_kernel<float>, dim3((unsigned)p.T), dim3(256), 0, st, (const float*)x_res,
                        (const float*)lw->norm_w, (float*)hn, (int)p.Dm, dims->layer_norm_eps);
   if (hipGetLastError() != hipSuccess) return JM_ERR_HIP;
-  if ((s = gemm(bf16, hn, p.Dm, lw->in_proj_w, p.Dm, xz, 2 * p.C, nullptr, 0, p.T, 2 * p.C, p.Dm, gws, st)) !=
-      JM_OK)
-    return s;
+  if ((s = gemm_launch(in_proj, hn, lw->in_proj_w, xz, nullptr, gws, st)) != JM_OK) return s;
   if ((s = jm::mixer_run(&p.md, &lw->mixer, xz, xz + p.C * p.esize, y, conv_in, conv_out, h0, h_out, mws,
                          mws_bytes, stream, decode, slots, pool, cu)) != JM_OK)
     return s;
-  return gemm(bf16, y, p.C, lw->out_proj_w, p.C, out, p.Dm, x_res, p.Dm, p.T, p.Dm, p.C, gws, st);
+  return gemm_launch(out_proj, y, lw->out_proj_w, out, x_res, gws, st);
 }
 
 }  // namespace
