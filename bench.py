@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the Jamba Mamba-1 mixer library on one MI355X.
 
-One step = one jm_mixer_prefill call over the 4K-token Jamba-v0.1 prefill (B=1, L=4096, d_inner=8192,
-d_state=16, dt_rank=256, bf16 I/O, fp32 state), i.e. every step of the mixer: conv1d + SiLU, x_proj,
-the dt/B/C RMSNorms, dt_proj + softplus, the selective scan, the D skip and the SiLU(z) gate.  Inputs are
-seeded synthetic tensors already resident in HBM.  W untimed warmup steps, then K timed steps between
-device synchronisations; value = tokens / second.  A second timed pass records HIP events between the
-library's kernels (jm_mixer_prefill_profiled) for the per-kernel roofline.  The decode workload (B=256,
-one token per sequence, the fp32 state rotated over 4 sets so that it streams from HBM) is timed the same
-way and reported alongside, as are the whole Mamba layer around the mixer and the serving-style calls
-(a packed batch of prompts of mixed lengths, decode over a state pool) and the gated scan's training
-forward and backward.  The fp64 CPU oracle is timed on the host on the same prefill workload as a
+One step = one jm_mixer_prefill call, i.e. every step of the mixer: conv1d + SiLU, x_proj, the dt/B/C
+RMSNorms, dt_proj + softplus, the selective scan, the D skip and the SiLU(z) gate.  The headline workload is
+the largest single-GPU one, the 256K-token context (B=1, L=262144, d_inner=8192, d_state=16, dt_rank=256,
+bf16 I/O, fp32 state); the 4K prefill (B=1), the batched prefill (B=8, L=4096) and the B=256 decode step are
+timed the same way and reported alongside.  Inputs are seeded synthetic tensors already resident in HBM.
+W untimed warmup steps, then K timed steps between device synchronisations (events on the stream the
+library launches on); value = tokens / second.  A second timed pass records HIP events between the
+library's kernels (jm_mixer_prefill_profiled) for the per-kernel roofline: the scan + gate step (its local,
+carry and full passes) against HBM with its fixed algorithmic bytes, its vector-ALU rate alongside.  The
+decode workload rotates its fp32 state over 4 sets so that it streams from HBM.  The whole Mamba layer
+around the mixer, the serving-style calls (a packed batch of prompts of mixed lengths, decode over a state
+pool), the exact-ZOH variant and the gated scan's training forward and backward are timed at the 4K shapes.
+The fp64 CPU oracle is timed first, on the host's cores, on a prefix of the headline workload as a
 baseline.
 
 Prints one JSON line.  Only one GPU is supported: --gpus N with N > 1 exits with a message.
@@ -32,10 +35,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 # fp32 vector ALU: 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T lane-operations/s (AMD's published
-# 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops).  Transcendentals (exp, rcp) issue at a quarter
-# of that rate, so each is counted as TRANS_SLOTS full-rate operations.
+# 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops).  Transcendentals (exp, rcp) issue at a lower
+# rate: a throughput probe on the box measured 18.6 T/s for v_exp_f32 against 59.5 T/s for v_fma_f32, so
+# each counts as TRANS_SLOTS full-rate operations.
 VALU_PEAK_TOPS = 78.6
-TRANS_SLOTS = 4
+TRANS_SLOTS = 3.2
 N_STATE_SETS = 4               # decode state sets rotated per step (4 x 140 MB > the 256 MB last-level cache)
 
 
@@ -126,7 +130,8 @@ def measured_traffic(workload: str, kernel: str):
     (the summary records the sha256 of the sources it measured)."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"{kernel}_B1_L4096_hbm_traffic.json")
+    short = workload.split("_", 2)[-1] if workload.startswith("jamba_prefill_") else workload
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{short}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     meta = json.load(open(path))
@@ -286,26 +291,72 @@ def time_decode(jm, cfg, steps, warmup, hip):
     return {"ms": ms, "stage_ms": stage_ms, "step_pct": percentiles(per_step)}
 
 
+# The CPU baseline's scan runs over channel blocks in forked workers (the recurrence is independent per
+# channel once delta, B and C are known); the parent sets this before forking and the workers write their
+# block of the output into a shared array.
+_CPU_JOB = {}
+
+
+def _cpu_scan_block(c0c1):
+    import numpy as np
+
+    import oracle
+    j = _CPU_JOB
+    c0, c1 = c0c1
+    y, _ = oracle.selective_scan(j["xc"][..., c0:c1], j["delta"][..., c0:c1], j["A_log"][c0:c1], j["bn"], j["cn"],
+                                 j["D"][c0:c1], None)
+    out = np.frombuffer(j["out"], dtype=np.float64).reshape(j["shape"])
+    out[..., c0:c1] = y * oracle.silu(j["z"][..., c0:c1])
+    return c1 - c0
+
+
 def cpu_baseline(cfg, max_tokens):
-    """The fp64 oracle (as it stands) on the host cores: the first max_tokens tokens of the workload."""
+    """The fp64 oracle (as it stands) on the host's cores, on the first max_tokens tokens of the workload (the
+    oracle's cost is linear in the tokens, so tokens/s on a prefix is its rate on the whole sequence).  The
+    conv, the projections and the norms run as the oracle's numpy calls, the matmuls on the BLAS threads;
+    the scan and the gate run as the oracle's own functions over channel blocks in one forked worker per
+    core.  Runs before anything touches the GPU."""
+    import multiprocessing as mp
+
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
     from jm_inputs import make_activations, make_weights, to_f64
 
+    cores = len(os.sched_getaffinity(0))
     w = {k: to_f64(v) for k, v in make_weights(cfg).items()}
-    a = make_activations(cfg, "cpu")
     L = min(cfg.seqlen, max_tokens)
-    x, z = to_f64(a["x"][:, :L]), to_f64(a["z"][:, :L])
-    t0 = time.perf_counter()
-    out, _, _ = oracle.mixer_prefill(x, z, w, cfg.dt_rank, cfg.d_state, cfg.norm_eps)
-    dt = time.perf_counter() - t0
-    assert np.isfinite(out).all()
+    a = make_activations(cfg, "cpu", seqlen=L)
+    x, z = to_f64(a["x"]), to_f64(a["z"])
+    del a
+    B, C = cfg.batch, cfg.d_inner
     blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": cfg.batch * L / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, prefill of the first {L} tokens of {cfg.name} (B={cfg.batch}, "
-                      f"C={cfg.d_inner}), {dt:.1f} s; matmuls on {blas} BLAS threads, the scan single-threaded"}
+    t0 = time.perf_counter()
+    xc, _ = oracle.causal_conv1d_silu(x, w["conv_w"], w["conv_b"], None)
+    dl, bv, cv = oracle.split_dbc(oracle.x_proj(xc, w["x_proj_w"]), cfg.dt_rank, cfg.d_state)
+    dln = oracle.rms_norm(dl, w["dt_norm_w"], cfg.norm_eps)
+    bn = oracle.rms_norm(bv, w["b_norm_w"], cfg.norm_eps)
+    cn = oracle.rms_norm(cv, w["c_norm_w"], cfg.norm_eps)
+    delta = oracle.dt_proj_softplus(dln, w["dt_proj_w"], w["dt_proj_b"])
+    t_front = time.perf_counter() - t0
+    shared = mp.RawArray("d", B * L * C)
+    _CPU_JOB.update(xc=xc, delta=delta, bn=bn, cn=cn, A_log=w["A_log"], D=w["D"], z=z, out=shared,
+                    shape=(B, L, C))
+    nblk = max(1, min(cores, C // 64))
+    edges = [C * i // nblk for i in range(nblk + 1)]
+    with mp.get_context("fork").Pool(nblk) as pool:
+        done = sum(pool.map(_cpu_scan_block, list(zip(edges[:-1], edges[1:]))))
+    dt = time.perf_counter() - t0
+    out = np.frombuffer(shared, dtype=np.float64).reshape(B, L, C)
+    assert done == C and np.isfinite(out).all()
+    _CPU_JOB.clear()
+    return {"value": B * L / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, prefill of the first {L} of the {cfg.seqlen} tokens of {cfg.name} "
+                      f"(B={B}, C={C}; the oracle is linear in the tokens), {dt:.1f} s: conv, projections and "
+                      f"norms {t_front:.1f} s with matmuls on {blas} BLAS threads, then the scan and gate over "
+                      f"{nblk} channel blocks in {nblk} forked workers; cores = the host cores this process may "
+                      f"use (sched_getaffinity)"}
 
 
 def time_layer(jm, cfg, steps, warmup, decode):
@@ -542,6 +593,54 @@ def run_decode(jm, dcfg, args, hip):
             "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()}}
 
 
+def run_prefill(jm, cfg, args, hip):
+    """One prefill workload: tokens/s, per-stage times against their algorithmic bytes, and the scan + gate
+    step against HBM (its roofline) with its vector-ALU rate alongside."""
+    import torch
+
+    log(f"prefill {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+    pre = time_prefill(jm, cfg, args.steps, args.warmup, hip)
+    torch.cuda.empty_cache()
+    B, L, C, N, R = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dt_rank
+    tokens = B * L
+    alg = algorithmic_bytes(B, L, C, N, R, 2)
+    groups = stage_groups(pre["stage_ms"])
+    stages = {}
+    for k, t in groups.items():
+        gbs = alg[k] / (t * 1e-3) / 1e9 if t > 0 else 0.0
+        stages[k] = {"us": round(t * 1e3, 2), "alg_bytes": alg[k], "GB_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    for k, t in pre["stage_ms"].items():
+        log(f"  {k:12s} {t * 1e3:9.2f} us")
+    xflops = 2.0 * tokens * (R + 2 * N) * C
+    stages["x_proj"]["mfma_tflops"] = round(xflops / (groups["x_proj"] * 1e-3) / 1e12, 2)
+    stages["x_proj"]["frac_mfma_bf16"] = round(stages["x_proj"]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    dflops = 2.0 * tokens * R * C
+    stages["norm_dt_proj"]["dt_proj_mfma_tflops"] = round(dflops / (pre["stage_ms"]["dt_proj"] * 1e-3) / 1e12, 2)
+    # the dominant step: scan + gate (the local, carry and full passes of one launch of the scan), against
+    # HBM with its fixed algorithmic bytes; its vector-ALU rate as a second figure
+    dom = max(groups, key=lambda k: groups[k])
+    ops = scan_alu_ops(B, L, C, N)
+    sg = groups["scan_gate"]
+    ach_alu = ops / (sg * 1e-3) / 1e12
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": stages[dom]["GB_s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": stages[dom]["frac_hbm"], "traffic": measured_traffic(cfg.name, dom),
+                "alg_bytes_per_launch": alg[dom], "us_per_launch": stages[dom]["us"]}
+    if dom == "scan_gate":
+        roofline["launch"] = "scan_local + scan_carry + scan_full (one scan of the step)"
+        roofline["alu"] = {"achieved": round(ach_alu, 2), "peak": VALU_PEAK_TOPS,
+                           "unit": f"T fp32 lane-ops/s (transcendental = {TRANS_SLOTS})",
+                           "frac": round(ach_alu / VALU_PEAK_TOPS, 4), "alg_ops_per_launch": int(ops)}
+    return {
+        "value": tokens / (pre["ms"] * 1e-3), "ms": pre["ms"],
+        "config": {"workload": f"{cfg.name}: Jamba-v0.1 Mamba mixer prefill", "batch": B, "seq_len": L,
+                   "d_inner": C, "d_state": N, "dt_rank": R, "d_conv": cfg.d_conv, "io": "bf16", "state": "fp32",
+                   "x_proj_splits": pre["splits"], "scan_pieces": pre["pieces"]},
+        "roofline": roofline, "stages": stages, "step_us_events": pre["step_pct"],
+        "mixer_GB_s": round(sum(alg.values()) / (pre["ms"] * 1e-3) / 1e9, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -549,9 +648,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--config", type=int, default=1, choices=(1, 2, 3),
-                    help="prefill workload: 1 = B1 L4096 (default), 2 = B8 L4096, 3 = B1 L262144")
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens of the headline workload the CPU oracle runs (a prefix; default 16384)")
+    ap.add_argument("--config", type=int, default=3, choices=(1, 2, 3),
+                    help="headline prefill workload: 3 = B1 L262144 (default), 1 = B1 L4096, 2 = B8 L4096")
+    ap.add_argument("--no-other-prefills", action="store_true",
+                    help="skip the prefill workloads other than the headline one")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
     ap.add_argument("--no-variants", action="store_true", help="skip the ZOH-variant prefill timing")
     ap.add_argument("--no-training", action="store_true",
@@ -562,6 +664,8 @@ def main():
                     help="skip the serving-style timings (packed prefill, pooled-state decode)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workload and print its figures (for per-workload profiles)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the headline prefill workload (for per-workload profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three device copies of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -570,11 +674,20 @@ def main():
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported",
               file=sys.stderr)
         sys.exit(2)
+    from jm_inputs import CONFIGS
+
+    only = args.decode_only or args.training_only or args.prefill_only
+    cfg = CONFIGS[args.config]
+    cpu = None
+    if not args.no_cpu_baseline and not only:
+        # before anything touches the GPU: the baseline forks its scan workers
+        log(f"cpu baseline: oracle on the first {min(args.cpu_tokens, cfg.seqlen)} tokens of {cfg.name} ...")
+        cpu = cpu_baseline(cfg, args.cpu_tokens)
+        log(f"  {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
 
     import torch
 
     import mamba_selective_scan_05_amd as jm
-    from jm_inputs import CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -594,71 +707,54 @@ def main():
     if args.training_only:
         print(json.dumps({"training": time_training(jm, args.steps, args.warmup)}), flush=True)
         return
-    cfg = CONFIGS[args.config]
-    log(f"prefill {cfg.name}: warmup {args.warmup}, steps {args.steps}")
-    pre = time_prefill(jm, cfg, args.steps, args.warmup, hip)
-    B, L, C, N, R = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dt_rank
-    tokens = B * L
-    value = tokens / (pre["ms"] * 1e-3)
-    alg = algorithmic_bytes(B, L, C, N, R, 2)
-    groups = stage_groups(pre["stage_ms"])
-    stages = {}
-    for k, t in groups.items():
-        gbs = alg[k] / (t * 1e-3) / 1e9 if t > 0 else 0.0
-        stages[k] = {"us": round(t * 1e3, 2), "alg_bytes": alg[k], "GB_s": round(gbs, 1),
-                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    for k, t in pre["stage_ms"].items():
-        log(f"  {k:12s} {t * 1e3:9.2f} us")
-    dom = max(groups, key=lambda k: groups[k])
-    if dom == "scan_gate":
-        # the scan is bound by the vector ALU (16 exponentials per token and channel), not by HBM
-        ops = scan_alu_ops(B, L, C, N)
-        ach = ops / (groups[dom] * 1e-3) / 1e12
-        roofline = {"bound": "alu", "kernel": dom, "achieved": round(ach, 2), "peak": VALU_PEAK_TOPS,
-                    "unit": "T fp32 lane-ops/s (transcendental = 4)", "frac": round(ach / VALU_PEAK_TOPS, 4),
-                    "traffic": measured_traffic(cfg.name, dom), "alg_ops_per_launch": ops,
-                    "alg_bytes_per_launch": alg[dom], "hbm_GB_s": stages[dom]["GB_s"],
-                    "us_per_launch": stages[dom]["us"]}
-    else:
-        ach = stages[dom]["GB_s"]
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
-                    "alg_bytes_per_launch": alg[dom], "us_per_launch": stages[dom]["us"]}
-    xflops = 2.0 * tokens * (R + 2 * N) * C
-    stages["x_proj"]["mfma_tflops"] = round(xflops / (groups["x_proj"] * 1e-3) / 1e12, 2)
-    stages["x_proj"]["frac_mfma_bf16"] = round(stages["x_proj"]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    head = run_prefill(jm, cfg, args, hip)
     result = {
         "metric": "mixer tokens/sec at d_inner=8192 (prefill & decode); achieved HBM GB/s % peak",
-        "value": round(value, 1),
+        "value": round(head["value"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(pre["ms"], 4),
+        "ms_per_step": round(head["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: Jamba-v0.1 Mamba mixer prefill", "batch": B, "seq_len": L,
-                   "d_inner": C, "d_state": N, "dt_rank": R, "d_conv": cfg.d_conv, "io": "bf16",
-                   "state": "fp32", "x_proj_splits": pre["splits"], "scan_pieces": pre["pieces"]},
-        "roofline": roofline,
-        "stages": stages,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "stages": head["stages"],
         # per-step times of the second (event-instrumented) pass: the events between kernels add a little
-        "step_us_events": pre["step_pct"],
-        "mixer_GB_s": round(sum(alg.values()) / (pre["ms"] * 1e-3) / 1e9, 1),
+        "step_us_events": head["step_us_events"],
+        "mixer_GB_s": head["mixer_GB_s"],
     }
+    if args.prefill_only:
+        print(json.dumps(result), flush=True)
+        return
+    if not args.no_other_prefills:
+        others = {}
+        for k in (1, 2, 3):
+            if k == args.config:
+                continue
+            r = run_prefill(jm, CONFIGS[k], args, hip)
+            others[CONFIGS[k].name] = {"tokens_per_s": round(r["value"], 1), "ms_per_step": round(r["ms"], 4),
+                                       "config": r["config"], "scan_gate": r["roofline"] if r["roofline"]["kernel"]
+                                       == "scan_gate" else None, "stages": r["stages"],
+                                       "mixer_GB_s": r["mixer_GB_s"]}
+        result["prefill_workloads"] = others
     if not args.no_decode:
         result["decode"] = run_decode(jm, CONFIGS[4], args, hip)
-    if not args.no_layer and args.config == 1:
+    one = CONFIGS[1]
+    pre1 = result.get("prefill_workloads", {}).get(one.name)
+    if not args.no_layer:
         from jm_inputs import LAYER_CONFIGS
         lay = {}
         for name, lcfg, dec in (("prefill", LAYER_CONFIGS[0], False), ("decode", LAYER_CONFIGS[1], True)):
             log(f"layer {lcfg.name}: warmup {args.warmup}, steps {args.steps}")
             lay[name] = time_layer(jm, lcfg, args.steps, args.warmup, dec)
-            # the mixer's share of the step, from the mixer-only timings above (prefill) or the decode entry
-            mix_us = pre["ms"] * 1e3 if name == "prefill" else result.get("decode", {}).get("us_per_step")
+            # the mixer's share of the step, from the mixer-only timings (4K prefill, decode)
+            mix_us = (pre1["ms_per_step"] * 1e3 if pre1 else (head["ms"] * 1e3 if args.config == 1 else None)) \
+                if name == "prefill" else result.get("decode", {}).get("us_per_step")
             if mix_us:
                 rest = lay[name]["us_per_step"] - mix_us
                 lay[name]["mixer_us"] = round(mix_us, 2)
@@ -668,29 +764,33 @@ def main():
                     lay[name]["gemm_tflops_estimate"] = round(tflops, 1)
             log(f"  {name}: {lay[name]['us_per_step']:.1f} us per step")
         result["layer"] = lay
-    if not args.no_serving and args.config == 1:
+    if not args.no_serving:
         result["serving"] = time_serving(jm, args.steps, args.warmup)
-        # the packed batch holds the same 4096 tokens as the B=1 prefill timed above
-        result["serving"]["varlen_prefill"]["vs_B1_L4096_prefill"] = round(
-            result["serving"]["varlen_prefill"]["tokens_per_s"] / value, 3)
+        # the packed batch holds the same 4096 tokens as the B=1 4K prefill
+        v1 = pre1["tokens_per_s"] if pre1 else (head["value"] if args.config == 1 else None)
+        if v1:
+            result["serving"]["varlen_prefill"]["vs_B1_L4096_prefill"] = round(
+                result["serving"]["varlen_prefill"]["tokens_per_s"] / v1, 3)
         if "decode" in result:
             result["serving"]["decode_slots"]["vs_plain_decode"] = round(
                 result["decode"]["us_per_step"] / result["serving"]["decode_slots"]["us_per_step"], 3)
-    if not args.no_variants and args.config == 1:
-        # the exact zero-order-hold input matrix instead of dt * B, same workload
-        log(f"prefill {cfg.name} with the exact ZOH input matrix: warmup {args.warmup}, steps {args.steps}")
-        zp = time_prefill(jm, cfg, args.steps, args.warmup, hip, zoh=True)
+    if not args.no_variants:
+        # the exact zero-order-hold input matrix instead of dt * B, on the 4K prefill
+        log(f"prefill {one.name} with the exact ZOH input matrix: warmup {args.warmup}, steps {args.steps}")
+        zp = time_prefill(jm, one, args.steps, args.warmup, hip, zoh=True)
         zg = stage_groups(zp["stage_ms"])
+        ztok = one.batch * one.seqlen
         result["variants"] = {"zoh_prefill": {
-            "workload": f"{cfg.name} with the exact zero-order-hold input matrix (exp(dt A) - 1) / A * B",
-            "us_per_step": round(zp["ms"] * 1e3, 2), "tokens_per_s": round(tokens / (zp["ms"] * 1e-3), 1),
-            "scan_gate_us": round(zg["scan_gate"] * 1e3, 2), "vs_default": round(pre["ms"] / zp["ms"], 3)}}
-    if not args.no_training and args.config == 1:
+            "workload": f"{one.name} with the exact zero-order-hold input matrix (exp(dt A) - 1) / A * B",
+            "us_per_step": round(zp["ms"] * 1e3, 2), "tokens_per_s": round(ztok / (zp["ms"] * 1e-3), 1),
+            "scan_gate_us": round(zg["scan_gate"] * 1e3, 2)}}
+        if pre1:
+            result["variants"]["zoh_prefill"]["vs_default"] = round(pre1["ms_per_step"] / zp["ms"], 3)
+    if not args.no_training:
         log(f"training (scan forward / backward): warmup {args.warmup}, steps {args.steps}")
         result["training"] = time_training(jm, args.steps, args.warmup)
-    if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {min(args.cpu_tokens, cfg.seqlen)} tokens ...")
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
