@@ -70,7 +70,8 @@ enum jm_status {
   JM_ERR_UNSUPPORTED = -2,  /* d_state != 16, d_conv != 4, d_inner % 64, dt_rank out of range, dtype */
   JM_ERR_ALIGNMENT = -3,    /* a pointer not 16-byte aligned, or a row stride not a multiple of 8   */
   JM_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than the matching *_workspace_size()       */
-  JM_ERR_HIP = -5           /* the HIP runtime reported an error when enqueueing a kernel           */
+  JM_ERR_HIP = -5,          /* the HIP runtime reported an error when enqueueing a kernel           */
+  JM_ERR_SCRATCH_LIMIT = -6 /* jm_mixer_decode_step_noalloc: the call exceeds its static scratch     */
 };
 
 enum jm_dtype { JM_F32 = 0, JM_BF16 = 1 };
@@ -158,6 +159,29 @@ int jm_mixer_decode_step(const jm_mixer_dims* dims, const jm_mixer_weights* weig
                          const void* conv_state_in, void* conv_state_out,
                          const float* ssm_state_in, float* ssm_state_out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode step that allocates nothing, for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  It is
+ * jm_mixer_decode_step with the same kernels and results, except that the intermediates live in a device
+ * array inside the library instead of a caller workspace:
+ *   - the array holds jm_mixer_decode_noalloc_scratch_limit() bytes (32 MiB) on each GPU the library runs
+ *     on, for the lifetime of the process; its address is looked up once per device, on the first call
+ *     made with that device current (hipGetSymbolAddress: no allocation);
+ *   - a call whose jm_mixer_decode_workspace_size(dims) exceeds the limit returns JM_ERR_SCRATCH_LIMIT with
+ *     nothing enqueued (at d_inner 8192, dt_rank 256 in bf16, up to 768 sequences fit);
+ *   - every call on one GPU shares that GPU's array and leaves its contents behind; the step needs nothing
+ *     in it to start at zero.  Calls that overlap on one GPU (concurrent streams or threads) race on the
+ *     array: serialise them, or use jm_mixer_decode_step with one workspace each.
+ * Arguments, layouts, aliasing and the other errors are those of jm_mixer_decode_step.
+ */
+int jm_mixer_decode_step_noalloc(const jm_mixer_dims* dims, const jm_mixer_weights* weights,
+                                 const void* x, const void* z, void* out,
+                                 const void* conv_state_in, void* conv_state_out,
+                                 const float* ssm_state_in, float* ssm_state_out, void* stream);
+
+/* Bytes of device scratch jm_mixer_decode_step_noalloc has on each GPU. */
+size_t jm_mixer_decode_noalloc_scratch_limit(void);
 
 /*
  * Decode step over a pool of per-sequence states: the decode step above, with sequence b's conv and SSM

@@ -17,6 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libjm_mixer.so")
 
 JM_OK, JM_ERR_INVALID_ARG, JM_ERR_UNSUPPORTED, JM_ERR_ALIGNMENT, JM_ERR_WORKSPACE, JM_ERR_HIP = 0, -1, -2, -3, -4, -5
+JM_ERR_SCRATCH_LIMIT = -6
 JM_F32, JM_BF16 = 0, 1
 JM_DISC_EULER, JM_DISC_ZOH = 0, 1
 
@@ -100,6 +101,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, V, V, V, S, V]
             f.restype = I
+        L.jm_mixer_decode_step_noalloc.argtypes = [P(Dims), P(Weights), V, V, V, V, V, V, V, V]
+        L.jm_mixer_decode_step_noalloc.restype = I
+        L.jm_mixer_decode_noalloc_scratch_limit.argtypes = []
+        L.jm_mixer_decode_noalloc_scratch_limit.restype = S
         L.jm_mixer_decode_step_slots.argtypes = [P(Dims), P(Weights), V, V, V, V, V, ctypes.c_int32, V, V, S, V]
         L.jm_mixer_decode_step_slots.restype = I
         L.jm_layer_decode_step_slots.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, ctypes.c_int32, V, V,
@@ -185,6 +190,17 @@ def call_decode_step(dims: Dims, weights: Weights, x, z, out, conv_in, conv_out,
                      stream: int) -> int:
     return lib().jm_mixer_decode_step(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in, h_out, ws,
                                       ws_bytes, stream)
+
+
+def call_decode_step_noalloc(dims: Dims, weights: Weights, x, z, out, conv_in, conv_out, h_in, h_out,
+                             stream: int) -> int:
+    """jm_mixer_decode_step_noalloc: the decode step with the library's own device scratch (no workspace)."""
+    return lib().jm_mixer_decode_step_noalloc(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in, h_out,
+                                              stream)
+
+
+def noalloc_scratch_limit() -> int:
+    return int(lib().jm_mixer_decode_noalloc_scratch_limit())
 
 
 def call_decode_step_slots(dims: Dims, weights: Weights, x, z, out, conv_pool, ssm_pool, pool_size: int, slots,

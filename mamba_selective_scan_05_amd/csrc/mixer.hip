@@ -4,8 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "jm_launch.h"
 #include "jm_mixer.h"
+
+// Device scratch of jm_mixer_decode_step_noalloc: its intermediates live here instead of in a caller's
+// workspace.  Each GPU the library runs on holds its own copy until the process ends; every call on a GPU
+// shares that GPU's copy.  Host code never uses this name as an address: the address of each device's copy
+// comes from hipGetSymbolAddress (static_scratch below).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -267,6 +276,25 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
 }
 
+// The address of this device's copy of `scratch`, looked up once per device with that device current (the
+// first jm_mixer_decode_step_noalloc call on it) and kept for the process's lifetime.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+int static_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return JM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return JM_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return JM_OK;
+}
+
 }  // namespace
 
 namespace jm {
@@ -332,6 +360,21 @@ int jm_mixer_decode_step(const jm_mixer_dims* dims, const jm_mixer_weights* weig
   return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
              workspace_bytes, stream, true);
 }
+
+int jm_mixer_decode_step_noalloc(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
+                                 const void* z, void* out, const void* conv_state_in, void* conv_state_out,
+                                 const float* ssm_state_in, float* ssm_state_out, void* stream) {
+  const int s = check_dims(dims, true);
+  if (s != JM_OK) return s;
+  if (make_plan(dims, true).total > (int64_t)kStaticScratchBytes) return JM_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const int r = static_scratch(&ws);
+  if (r != JM_OK) return r;
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, ws,
+             kStaticScratchBytes, stream, true);
+}
+
+size_t jm_mixer_decode_noalloc_scratch_limit(void) { return kStaticScratchBytes; }
 
 int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
                                const void* z, void* out, void* conv_state_pool, float* ssm_state_pool,
@@ -418,6 +461,9 @@ const char* jm_status_string(int status) {
     case JM_ERR_ALIGNMENT: return "misaligned pointer (16 bytes required) or row stride (multiple of 8)";
     case JM_ERR_WORKSPACE: return "workspace missing or too small";
     case JM_ERR_HIP: return "HIP runtime error while enqueueing a kernel";
+    case JM_ERR_SCRATCH_LIMIT: return "the call needs more than the 32 MiB of device scratch that "
+                                      "jm_mixer_decode_step_noalloc has (fewer sequences per call, or use "
+                                      "jm_mixer_decode_step with a workspace)";
     default: return "unknown status";
   }
 }

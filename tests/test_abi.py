@@ -262,3 +262,17 @@ def test_module_level_mixer_reads_dims_from_weight_shapes():
     assert (m.d_inner, m.dt_rank, m.d_state, m.d_conv, m.eps, m.zoh) == (128, 24, 16, 4, 1e-5, True)
     d = m.dims(3, 9)
     assert (d.batch, d.seqlen, d.d_inner, d.dt_rank, d.discretization) == (3, 9, 128, 24, jm.JM_DISC_ZOH)
+
+
+def test_noalloc_decode_rejects_calls_beyond_its_scratch_before_launch():
+    # a decode batch whose workspace exceeds the static scratch: rejected before any HIP call
+    limit = jm.noalloc_scratch_limit()
+    assert limit == 32 << 20
+    small = _dims(batch=256, seqlen=1, d_inner=8192, dt_rank=256, io_dtype=jm.JM_BF16)
+    big = _dims(batch=4096, seqlen=1, d_inner=8192, dt_rank=256, io_dtype=jm.JM_BF16)
+    assert jm.decode_workspace_size(small) <= limit < jm.decode_workspace_size(big)
+    args = [FAKE] * 7 + [0]
+    assert jm.call_decode_step_noalloc(big, _weights(), *args) == _lib.JM_ERR_SCRATCH_LIMIT
+    assert "32 MiB" in jm.status_string(_lib.JM_ERR_SCRATCH_LIMIT)
+    # dims errors come first, as in jm_mixer_decode_step
+    assert jm.call_decode_step_noalloc(_dims(d_state=8), _weights(), *args) == _lib.JM_ERR_UNSUPPORTED
