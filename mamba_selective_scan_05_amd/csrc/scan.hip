@@ -19,6 +19,10 @@
 //   full   : every piece reruns from its incoming state, producing the gated output; the last piece
 //            writes the final SSM state and the conv state.
 // With P = 1 only the full pass runs.
+//
+// A workgroup holds up to four waves: adjacent 64-channel groups of the same piece, one per SIMD of a CU, so
+// that the four share the piece's B / C rows in the CU's scalar cache (measured against one-wave workgroups:
+// the 256K prefill's local pass 15% faster, the whole scan 8%).
 #include "jm_device.h"
 #include "jm_launch.h"
 
@@ -28,6 +32,7 @@ namespace {
 
 constexpr int kN = 16;
 constexpr int kTaps = 4;
+constexpr int kMaxScanWaves = 4;   // waves per workgroup of the local and full passes
 constexpr int kBatch = 4;   // tokens per prefetch batch (keeps the pass under 128 VGPRs: 4 waves per SIMD)
 // s_waitcnt operand (gfx9 encoding): scalar-memory count 0, vector-memory and export counts at their maxima
 constexpr int kWaitScalar = 0xC07F;
@@ -76,7 +81,10 @@ __device__ __forceinline__ void load_a2(const T* A_log, int c, float* a2) {
 // and registers through a 4 KB LDS tile, as four 1 KB rows of contiguous 16-byte lanes: per-lane 64-byte
 // strides would make each 16-byte access instruction touch 32 cache lines for 1 KB of data (this is the
 // whole traffic of a one-token step).  In LDS, chunk q of lane l sits in slot q ^ ((l >> 2) & 3) of the
-// lane's 64 bytes, which keeps the per-lane 16-byte reads and writes free of bank conflicts.
+// lane's 64 bytes, which keeps the per-lane 16-byte reads and writes free of bank conflicts.  The HBM side
+// uses non-temporal loads and stores: a state is read once and written once per call, and keeping it out
+// of the caches leaves them to the weights and activations that are reused (the B = 256 decode step went
+// from 86 to 75 us with its four state sets rotated, i.e. with cold states).
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 __device__ __forceinline__ int hslot(int l, int q) { return l * 16 + ((q ^ ((l >> 2) & 3)) << 2); }
 __device__ __forceinline__ void state_load(const float* src, float* hs, int lane, float* h) {
@@ -84,7 +92,8 @@ __device__ __forceinline__ void state_load(const float* src, float* hs, int lane
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int g = q * 64 + lane;                      // 16-byte chunk g of the wave's 4 KB
-    *reinterpret_cast<f32x4*>(&hs[hslot(g >> 2, g & 3)]) = *reinterpret_cast<const f32x4*>(src + g * 4);
+    *reinterpret_cast<f32x4*>(&hs[hslot(g >> 2, g & 3)]) =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + g * 4));
   }
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -103,7 +112,8 @@ __device__ __forceinline__ void state_store(float* dst, float* hs, int lane, con
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int g = q * 64 + lane;
-    *reinterpret_cast<f32x4*>(dst + g * 4) = *reinterpret_cast<const f32x4*>(&hs[hslot(g >> 2, g & 3)]);
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&hs[hslot(g >> 2, g & 3)]),
+                                 reinterpret_cast<f32x4*>(dst + g * 4));
   }
 }
 
@@ -114,15 +124,20 @@ __device__ __forceinline__ void state_store(float* dst, float* hs, int lane, con
 // stores a sequence's final state where it ends.
 // ZOH: the input matrix is the exact zero-order hold instead of dt * B (a variant of the same recurrence).
 // SAVE (full pass of a plain batch): also write the state entering every backward piece, for the backward.
+// A workgroup is blockDim.x / 64 waves over adjacent 64-channel groups; each wave has its own 4 KB LDS tile
+// in the dynamic shared memory (blockDim.x / 64 tiles).
 template <typename T, bool FULL, bool VAR, bool ZOH = false, bool SAVE = false>
-__global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
-  const int c = blockIdx.x * 64 + threadIdx.x;
+__global__ __launch_bounds__(kMaxScanWaves * 64) void scan_pass_kernel(ScanArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int cg = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);   // the wave's 64-channel group
+  const int c = cg * 64 + lane;
   const int p = blockIdx.y;
   const int b = blockIdx.z;
   const int L = a.L, C = a.C, P = a.P;
   const int t0 = p * a.Lp, t1 = min(L, t0 + a.Lp);
 
-  __shared__ __attribute__((aligned(16))) float hs[64 * kN];
+  extern __shared__ __attribute__((aligned(16))) float scan_tiles[];
+  float* hs = scan_tiles + (threadIdx.x >> 6) * 64 * kN;
   float a2[kN], h[kN];
   load_a2((const T*)a.A_log, c, a2);
   float Av[ZOH ? kN : 1], iA[ZOH ? kN : 1];
@@ -145,7 +160,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   }
   auto init_state = [&](int64_t row) __attribute__((always_inline)) {
     if (a.h0 && row >= 0) {
-      state_load(a.h0 + (row * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+      state_load(a.h0 + (row * C + cg * 64) * kN, hs, lane, h);
     } else {
 #pragma unroll
       for (int n = 0; n < kN; ++n) h[n] = 0.0f;
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
       const int u1 = min(max(end, u + 1), n_tok);
       run_range(u, u1);
       if (FULL && end <= n_tok && srow >= 0)      // the sequence ends in this piece
-        state_store(a.h_out + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+        state_store(a.h_out + (srow * C + cg * 64) * kN, hs, lane, h);
       u = u1;
       if (u >= n_tok) break;
       s = seq_of(a.cu, a.nseq, t0 + u);            // the next non-empty sequence starts at u
@@ -368,7 +383,7 @@ __global__ __launch_bounds__(64) void scan_pass_kernel(ScanArgs a) {
   }
   if (!VAR && p == P - 1) {
     if (srow < 0) return;
-    state_store(a.h_out + (srow * C + blockIdx.x * 64) * kN, hs, threadIdx.x, h);
+    state_store(a.h_out + (srow * C + cg * 64) * kN, hs, lane, h);
     // conv state (unless the conv step wrote it): the last K-1 entries of the extended input (old state
     // entries when L < K-1).  All three are read before any is written, so conv_out may alias conv_in.
     if (!a.conv_out) return;
@@ -441,15 +456,21 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
   }
 }
 
+// Waves per workgroup of the passes: four when d_inner allows it (a multiple of 256), else two or one.
+int scan_waves(int C) { return C % (64 * 4) == 0 ? 4 : C % (64 * 2) == 0 ? 2 : 1; }
+
 template <typename T, bool VAR, bool ZOH>
 void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
+  const int wpb = scan_waves(a.C);
+  const dim3 block(64 * wpb);
+  const size_t lds = (size_t)wpb * 64 * kN * sizeof(float);
   auto mark = [&](int i) {
     if (marks) (void)hipEventRecord((hipEvent_t)marks[i], st);
   };
   mark(0);
   if (a.P > 1) {
-    dim3 gl(a.C / 64, a.P - 1, a.B);
-    hipLaunchKernelGGL((scan_pass_kernel<T, false, VAR, ZOH>), gl, dim3(64), 0, st, a);
+    dim3 gl(a.C / (64 * wpb), a.P - 1, a.B);
+    hipLaunchKernelGGL((scan_pass_kernel<T, false, VAR, ZOH>), gl, block, lds, st, a);
   }
   mark(1);
   if (a.P > 1) {
@@ -458,14 +479,14 @@ void run_scan(const ScanArgs& a, hipStream_t st, void* const* marks) {
                        (const T*)a.A_log, a.h0, a.cin, a.B, a.C, a.P, a);
   }
   mark(2);
-  dim3 gf(a.C / 64, a.P, a.B);
+  dim3 gf(a.C / (64 * wpb), a.P, a.B);
   if constexpr (!VAR && !ZOH) {
     if (a.saved) {
-      hipLaunchKernelGGL((scan_pass_kernel<T, true, false, false, true>), gf, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((scan_pass_kernel<T, true, false, false, true>), gf, block, lds, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((scan_pass_kernel<T, true, VAR, ZOH>), gf, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((scan_pass_kernel<T, true, VAR, ZOH>), gf, block, lds, st, a);
 }
 
 template <typename T>
@@ -484,13 +505,15 @@ void run_scan_t(const ScanArgs& a, hipStream_t st, void* const* marks) {
 void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st) {
   if (a.P <= 1) return;
   const int64_t n = (int64_t)a.B * kN * a.C;
-  dim3 gl(a.C / 64, a.P - 1, a.B);
+  const int wpb = scan_waves(a.C);
+  const size_t lds = (size_t)wpb * 64 * kN * sizeof(float);
+  dim3 gl(a.C / (64 * wpb), a.P - 1, a.B);
   if (bf16) {
-    hipLaunchKernelGGL((scan_pass_kernel<bf16_t, false, false>), gl, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((scan_pass_kernel<bf16_t, false, false>), gl, dim3(64 * wpb), lds, st, a);
     hipLaunchKernelGGL((scan_carry_kernel<bf16_t, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.loc,
                        (const bf16_t*)a.A_log, a.h0, a.cin, a.B, a.C, a.P, a);
   } else {
-    hipLaunchKernelGGL((scan_pass_kernel<float, false, false>), gl, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((scan_pass_kernel<float, false, false>), gl, dim3(64 * wpb), lds, st, a);
     hipLaunchKernelGGL((scan_carry_kernel<float, false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.loc,
                        (const float*)a.A_log, a.h0, a.cin, a.B, a.C, a.P, a);
   }
