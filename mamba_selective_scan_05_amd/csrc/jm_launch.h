@@ -38,16 +38,17 @@ void launch_conv_step(bool bf16, const void* x, int64_t x_stride, const void* co
                       const void* conv_state_in, void* xc, void* conv_state_out, int B, int C, hipStream_t st,
                       const int32_t* slots = nullptr, int pool = 0);
 
-// Tokens per x_proj workgroup tile (bf16 path), and the number of column groups (grid z) for N columns in
-// the wide (288 columns per workgroup) or narrow (32) layout.
-int xproj_token_tile();
+// Tokens per x_proj workgroup tile (bf16 path: 128, or 256 in the tall layout for long inputs), and the
+// number of column groups (grid z) for N columns in the wide or tall (288 columns per workgroup) or narrow
+// (32) layout.
+int xproj_token_tile(bool tall = false);
 int xproj_column_groups(int N, bool narrow);
 // Most channel slices the x_proj contraction may be split over (the norm step adds at most this many).
 constexpr int kMaxXprojSplits = 16;
 
 // dbc partial sums: part[s, m, n] = sum over channel slice s of xc[m, k] * w[n, k].
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
-                  bool narrow, hipStream_t st);
+                  bool narrow, hipStream_t st, bool tall = false);
 
 // Sum the partials in slice order, RMSNorm the dt / B / C slices -> dln [M, R] (io dtype), bc [M, 2N].
 void launch_norm(bool bf16, const float* part, int splits, int M, int R, int N, const void* dt_norm_w,
@@ -99,6 +100,14 @@ struct ScanArgs {
 void launch_scan(bool bf16, const ScanArgs& a, hipStream_t st, void* const* marks = nullptr);
 // Only the local and carry passes (P > 1): every piece's incoming state -> a.cin.
 void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st);
+
+// The layer's projections for at most 256 tokens, bf16: Y[m, n] = sum_k X[m, k] W[n, k] (+ R[m, n]), row
+// strides ldx / ldw / ldr / ldy in elements (multiples of 8).  skinny_gemm_splits gives the K split for a
+// shape (0: the shape is not supported: M > 256, N or K not a multiple of 64); with more than one split the
+// fp32 partial sums take splits * M * N * 4 bytes of `part`, within ws_bytes.  R may alias Y.
+int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes);
+void launch_skinny_gemm(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* R, int64_t ldr, void* Y,
+                        int64_t ldy, int M, int N, int K, int splits, float* part, hipStream_t st);
 
 // Scan pieces for B sequences of L tokens over C channels: about a fixed number of waves in the full pass,
 // pieces of at least 128 tokens, each piece's rows (row_bytes apart) under 2 GiB.

@@ -1,6 +1,7 @@
 // The whole Jamba Mamba layer around the mixer (jm_layer.h): pre-norm RMSNorm, in_proj, the mixer,
-// out_proj and the residual add.  The two projections are plain GEMMs and go to hipBLASLt; the norm is a
-// kernel here; the mixer is this library's own.
+// out_proj and the residual add.  The two projections are plain GEMMs: for a decode-sized batch (at most 256
+// tokens, bf16) they run on this library's weight-streaming kernel (gemm_skinny.hip), otherwise through
+// hipBLASLt; the norm is a kernel here; the mixer is this library's own.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 #include <stdint.h>
@@ -219,10 +220,16 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
     return jm::mixer_run(&p.md, &lw->mixer, nullptr, nullptr, nullptr, conv_in, conv_out, h0, h_out, mws,
                          mws_bytes, stream, decode, slots, pool, cu);
   }
-  // both GEMMs resolved (handle, descriptors, algorithm) before anything is enqueued
+  // A decode-sized batch (at most 256 tokens, bf16) runs both projections on the weight-streaming kernel
+  // (gemm_skinny.hip); otherwise both GEMMs are resolved in hipBLASLt (handle, descriptors, algorithm)
+  // before anything is enqueued.
+  const int sp_in = bf16 ? jm::skinny_gemm_splits((int)p.T, (int)(2 * p.C), (int)p.Dm, kGemmWorkspace) : 0;
+  const int sp_out = bf16 ? jm::skinny_gemm_splits((int)p.T, (int)p.Dm, (int)p.C, kGemmWorkspace) : 0;
   Gemm in_proj, out_proj;
-  if ((s = gemm_prepare(&in_proj, bf16, p.Dm, p.Dm, 2 * p.C, false, 0, p.T, 2 * p.C, p.Dm)) != JM_OK) return s;
-  if ((s = gemm_prepare(&out_proj, bf16, p.C, p.C, p.Dm, true, p.Dm, p.T, p.Dm, p.C)) != JM_OK) return s;
+  if (!sp_in && (s = gemm_prepare(&in_proj, bf16, p.Dm, p.Dm, 2 * p.C, false, 0, p.T, 2 * p.C, p.Dm)) != JM_OK)
+    return s;
+  if (!sp_out && (s = gemm_prepare(&out_proj, bf16, p.C, p.C, p.Dm, true, p.Dm, p.T, p.Dm, p.C)) != JM_OK)
+    return s;
   (void)hipGetLastError();
   if (bf16)
     hipLaunchKernelGGL(rms_norm_kernel<jm::bf16_t>, dim3((unsigned)p.T), dim3(256), 0, st,
@@ -232,10 +239,21 @@ int layer_run(const jm_layer_dims* dims, const jm_layer_weights* lw, const void*
     hipLaunchKernelGGL(rms_norm_kernel<float>, dim3((unsigned)p.T), dim3(256), 0, st, (const float*)x_res,
                        (const float*)lw->norm_w, (float*)hn, (int)p.Dm, dims->layer_norm_eps);
   if (hipGetLastError() != hipSuccess) return JM_ERR_HIP;
-  if ((s = gemm_launch(in_proj, hn, lw->in_proj_w, xz, nullptr, gws, st)) != JM_OK) return s;
+  if (sp_in) {
+    jm::launch_skinny_gemm(hn, p.Dm, lw->in_proj_w, p.Dm, nullptr, 0, xz, 2 * p.C, (int)p.T, (int)(2 * p.C),
+                           (int)p.Dm, sp_in, (float*)gws, st);
+    if (hipGetLastError() != hipSuccess) return JM_ERR_HIP;
+  } else if ((s = gemm_launch(in_proj, hn, lw->in_proj_w, xz, nullptr, gws, st)) != JM_OK) {
+    return s;
+  }
   if ((s = jm::mixer_run(&p.md, &lw->mixer, xz, xz + p.C * p.esize, y, conv_in, conv_out, h0, h_out, mws,
                          mws_bytes, stream, decode, slots, pool, cu)) != JM_OK)
     return s;
+  if (sp_out) {
+    jm::launch_skinny_gemm(y, p.C, lw->out_proj_w, p.C, x_res, p.Dm, out, p.Dm, (int)p.T, (int)p.Dm, (int)p.C,
+                           sp_out, (float*)gws, st);
+    return hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
+  }
   return gemm_launch(out_proj, y, lw->out_proj_w, out, x_res, gws, st);
 }
 

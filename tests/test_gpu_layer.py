@@ -80,6 +80,16 @@ def test_layer_jamba_widths_512_tokens():
     _check_prefill(cfg, False)
 
 
+@pytest.mark.parametrize("B,L", [(2, 100), (1, 1), (1, 256)])
+def test_layer_prefill_up_to_256_tokens_in_place(B, L):
+    # at most 256 tokens in bf16: both projections run on the library's weight-streaming kernel; d_inner 1024
+    # against d_model 128 splits out_proj's K range (fp32 partials added by the reduce kernel, with the
+    # residual read from the output buffer itself)
+    cfg = MixerConfig(f"layer_skinny_B{B}_L{L}", batch=B, seqlen=L, d_inner=1024, dt_rank=64, io_dtype="bf16",
+                      seed=35, d_model=128)
+    _check_prefill(cfg, True, in_place=True)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_layer_decode_steps(io):
     cfg = MixerConfig(f"layer_decode_{io}", batch=3, seqlen=1, d_inner=128, dt_rank=16, io_dtype=io, seed=33,
