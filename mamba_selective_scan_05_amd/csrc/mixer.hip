@@ -33,6 +33,9 @@ constexpr int64_t kScanWaveTarget = JM_SCAN_WAVE_TARGET;
 constexpr int kMinPiece = 128;
 // x_proj: split the contraction over channel slices until there are this many workgroups (one per CU).
 constexpr int kXprojWgTarget = 256;
+// x_proj takes 256-token tiles from this many tokens on (fewer re-reads of W_x; shorter inputs keep 128-token
+// tiles, which need half as many channel slices and partial sums to fill the GPU).
+constexpr int64_t kXprojTallTokens = 32768;
 
 struct Plan {
   int B, L, C, N, R, W;
@@ -41,6 +44,7 @@ struct Plan {
   int esize;
   int splits;    // x_proj channel slices
   bool narrow;   // x_proj in 32-column groups (few tokens)
+  bool tall;     // x_proj in 256-token tiles (long inputs)
   int P, Lp;     // scan pieces per sequence, tokens per piece
   int64_t xs, zs;
   int nseq;      // packed batches: number of sequences (the plan itself runs B = 1 over L = all tokens)
@@ -98,8 +102,9 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
   // the most slices leave the GPU short of workgroups, the narrow column layout multiplies the grid.
   p.splits = 1;
   p.narrow = false;
+  p.tall = p.bf16 && p.T >= kXprojTallTokens;
   if (p.bf16) {
-    const int64_t tile = jm::xproj_token_tile();
+    const int64_t tile = jm::xproj_token_tile(p.tall);
     const int64_t mtiles = (p.T + tile - 1) / tile;
     auto grow = [&](int64_t groups) {
       p.splits = 1;
@@ -234,7 +239,7 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
     if (varlen) jm::launch_varlen_states(p.bf16, x, p.xs, conv_in, conv_out, h0, h_out, p.C, p.L, vs, st);
   }
   marks.mark(1);
-  jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st);
+  jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st, p.tall);
   marks.mark(2);
   jm::launch_norm(p.bf16, dbc, p.splits, (int)p.T, p.R, p.N, w->dt_norm_w, w->b_norm_w, w->c_norm_w,
                   dims->norm_eps, dln, bc, st);
@@ -447,7 +452,7 @@ int jm_mixer_prefill_workspace_layout(const jm_mixer_dims* dims, jm_workspace_la
   layout->dbc_splits = p.splits;
   layout->scan_chunks = p.P;
   layout->total_bytes = p.total;
-  layout->xproj_path = !p.bf16 ? 2 : p.narrow ? 1 : 0;
+  layout->xproj_path = !p.bf16 ? 2 : p.narrow ? 1 : p.tall ? 3 : 0;
   layout->reserved = 0;
   return JM_OK;
 }

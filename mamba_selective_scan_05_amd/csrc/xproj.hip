@@ -164,6 +164,112 @@ __global__ __launch_bounds__(kThreads) void xproj_mfma_kernel(const bf16_t* __re
   }
 }
 
+// Long inputs: 256-token x 288-column tiles per workgroup of 8 waves (wave (mg, ng) computes rows
+// [64 mg, 64 mg + 64) x column tiles [9 ng, 9 ng + 9)), so W_x is read once per 256 tokens instead of once per
+// 128: the operands reach LDS through the direct global-to-LDS path, whose delivery rate from L2 bounds
+// this kernel, and W_x is most of what it delivers (4.7 MB per token tile against 4 MB of xc per 256
+// tokens).  Two LDS stages of one 64-wide K block each (144 KB: 32 KB of xc, 40 KB of W_x rows padded to
+// 320 so that every wave issues five loads; the padding rows re-read the last row and are never used).
+constexpr int kMT2 = 256;
+constexpr int kNB2 = 320;          // W_x rows loaded per K block (kNG = 288 used)
+constexpr int kThreads2 = 512;
+
+__global__ __launch_bounds__(kThreads2) void xproj_mfma_tall_kernel(const bf16_t* __restrict__ xc,
+                                                                    const bf16_t* __restrict__ w,
+                                                                    float* __restrict__ part, int M, int N,
+                                                                    int K, int splits) {
+  constexpr int kNT = kNTWide;
+  constexpr int kAL = kMT2 / 8 / 8;   // direct loads per wave per block
+  constexpr int kBL = kNB2 / 8 / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t As0[kMT2 * kKB], As1[kMT2 * kKB];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs0[kNB2 * kKB], Bs1[kNB2 * kKB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.x % splits;
+  const int m0 = (blockIdx.x / splits) * kMT2;
+  const int n0 = blockIdx.z * 32 * kNT;
+  const int kps = K / splits;
+  const int kbeg = s * kps;
+  const int nblocks = kps / kKB;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int mg = wave & 3, ng = wave >> 2;
+
+  f32x4 acc[4][kNT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const char* abase = reinterpret_cast<const char*>(xc + (int64_t)m0 * K);
+  const char* bbase = reinterpret_cast<const char*>(w + (int64_t)n0 * K);
+  uint32_t oa[kAL], ob[kBL];
+#pragma unroll
+  for (int q = 0; q < kAL; ++q) {
+    const int row = (wave * kAL + q) * 8 + (lane >> 3);
+    oa[q] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + (((lane & 7) ^ (row & 7)) << 3)) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < kBL; ++q) {
+    const int row = (wave * kBL + q) * 8 + (lane >> 3);
+    ob[q] = (uint32_t)(((int64_t)(min(n0 + row, N - 1) - n0) * K + (((lane & 7) ^ (row & 7)) << 3)) * 2);
+  }
+  auto issue = [&](int b, bf16_t* A, bf16_t* B) {
+    const int64_t kb = (int64_t)(kbeg + min(b, nblocks - 1) * kKB) * 2;
+#pragma unroll
+    for (int q = 0; q < kBL; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(bbase + kb + ob[q]),
+                                       (lds_void_t*)(B + (wave * kBL + q) * 8 * kKB), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kAL; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(abase + kb + oa[q]),
+                                       (lds_void_t*)(A + (wave * kAL + q) * 8 * kKB), 16, 0, 0);
+  };
+  auto compute = [&](const bf16_t* A, const bf16_t* B) {
+#pragma unroll
+    for (int ks = 0; ks < kKB / 8; ks += 4) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = lds_frag(&A[swz(mg * 64 + r * 16 + lr, ks + lk)]);
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        const bf16x8 bv = lds_frag(&B[swz((ng * kNT + t) * 16 + lr, ks + lk)]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], bv, acc[r][t], 0, 0, 0);
+      }
+    }
+  };
+  // Block b: wait for this thread's loads of block b, barrier (everyone's have landed, and everyone is done
+  // with block b - 1), refill block b - 1's stage with block b + 1, multiply block b.
+  issue(0, As0, Bs0);
+  auto step = [&](int b, const bf16_t* A, const bf16_t* B, bf16_t* An, bf16_t* Bn) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    stage_barrier();
+    issue(b + 1, An, Bn);
+    compute(A, B);
+  };
+  for (int b = 0;; b += 2) {
+    step(b, As0, Bs0, As1, Bs1);
+    if (b + 1 >= nblocks) break;
+    step(b + 1, As1, Bs1, As0, Bs0);
+    if (b + 2 >= nblocks) break;
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+
+  float* dst = part + (int64_t)s * M * N;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    const int n = n0 + (ng * kNT + t) * 16 + lr;
+    if (n >= N) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + mg * 64 + r * 16 + (lane >> 4) * 4 + i;
+        if (m < M) dst[(int64_t)m * N + n] = acc[r][t][i];
+      }
+  }
+}
+
 // fp32: one thread per (m, n); the xc row is staged through LDS in 1024-element pieces.
 __global__ __launch_bounds__(64) void xproj_f32_kernel(const float* __restrict__ xc, const float* __restrict__ w,
                                                        float* __restrict__ part, int M, int N, int K) {
@@ -184,7 +290,7 @@ __global__ __launch_bounds__(64) void xproj_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-int xproj_token_tile() { return kMT; }
+int xproj_token_tile(bool tall) { return tall ? kMT2 : kMT; }
 
 int xproj_column_groups(int N, bool narrow) {
   const int cols = 32 * (narrow ? kNTNarrow : kNTWide);
@@ -192,8 +298,14 @@ int xproj_column_groups(int N, bool narrow) {
 }
 
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
-                  bool narrow, hipStream_t st) {
+                  bool narrow, hipStream_t st, bool tall) {
   if (M == 0) return;
+  if (bf16 && tall) {
+    dim3 grid(((M + kMT2 - 1) / kMT2) * splits, 1, xproj_column_groups(N, false));
+    hipLaunchKernelGGL(xproj_mfma_tall_kernel, grid, dim3(kThreads2), 0, st, (const bf16_t*)xc, (const bf16_t*)w,
+                       part, M, N, K, splits);
+    return;
+  }
   if (bf16) {
     dim3 grid(((M + kMT - 1) / kMT) * splits, 1, xproj_column_groups(N, narrow));
     if (narrow)

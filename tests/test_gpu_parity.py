@@ -94,6 +94,16 @@ def test_bf16_wide_xproj_tiles_across_sequences(with_state):
     _run_and_check(cfg, with_state=with_state, row_stride=528)
 
 
+@pytest.mark.parametrize("R", [16, 512])
+def test_bf16_tall_xproj_ragged(R):
+    # 32768 tokens or more: x_proj takes 256-token tiles (eight waves, two LDS stages); 40000 tokens leave a
+    # ragged last tile of 64, dt_rank 512 makes two 288-column groups
+    import mamba_selective_scan_05_amd as jm
+    cfg = _small(f"tall_xproj_R{R}", 1, 40000, 256, R, "bf16", 23)
+    assert jm.workspace_layout(jm.make_dims(1, 40000, 256, R, jm.JM_BF16)).xproj_path == 3
+    _run_and_check(cfg)
+
+
 @pytest.mark.parametrize("B,L", [(1, 450), (2, 155)])
 def test_bf16_few_token_tiles_dt_proj(B, L):
     # at most 8 64-token tiles: dt_proj takes 128-channel workgroups; at d_inner 8192 they hold two tiles
