@@ -114,10 +114,7 @@ void launch_skinny_gemm(const void* X, int64_t ldx, const void* W, int64_t ldw, 
 void scan_plan(int B, int L, int C, int64_t row_bytes, int* P, int* Lp);
 
 // Backward of the gated scan (training).  Pieces of kBwdPiece tokens; all [B*L, C] tensors contiguous.
-#ifndef JM_BWD_PIECE
-#define JM_BWD_PIECE 32
-#endif
-constexpr int kBwdPiece = JM_BWD_PIECE;
+constexpr int kBwdPiece = 32;
 struct BwdArgs {
   const void* xc;        // [B*L, C] io dtype
   const void* delta;     // [B*L, C]

@@ -25,11 +25,10 @@ constexpr int64_t kAlign = 256;
 constexpr int kMaxSeqlen = 1 << 21;   // tokens of a prefill call (the conv's grid rows stay within 65536)
 constexpr int kMaxBatch = 1 << 16;    // sequences of a call (they index the grid's y / z axes, at most 65536)
 
-// Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.
-#ifndef JM_SCAN_WAVE_TARGET
-#define JM_SCAN_WAVE_TARGET 6144
-#endif
-constexpr int64_t kScanWaveTarget = JM_SCAN_WAVE_TARGET;
+// Scan pieces: aim for this many 64-lane waves in the full pass (six per SIMD, the full pass's occupancy), with
+// pieces of at least kMinPiece tokens.  Measured against 4096, 2048 and 1024 waves: fewer pieces do less
+// local-pass work but leave the vector ALU idle (one wave per SIMD runs a token 2.3 times slower).
+constexpr int64_t kScanWaveTarget = 6144;
 constexpr int kMinPiece = 128;
 // x_proj: split the contraction over channel slices until there are this many workgroups (one per CU).
 constexpr int kXprojWgTarget = 256;

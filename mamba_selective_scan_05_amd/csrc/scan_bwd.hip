@@ -32,20 +32,8 @@ constexpr int kQ = 4;                  // states per lane
 // Tile sizes measured at B=1, L=4096, d_inner 8192 (bf16): sub-chunks of 4 tokens in pieces of 32 at four
 // waves per SIMD took 1073 us for the whole backward, against 1106 (8 / 64, two waves), 1174 (4 / 16) and
 // 1244 (8 / 32, three waves); keeping the decay factors and prefetching every input won over recomputing.
-#ifndef JM_BWD_SUB
-#define JM_BWD_SUB 4
-#endif
-#ifndef JM_BWD_WAVES_PER_SIMD
-#define JM_BWD_WAVES_PER_SIMD 4
-#endif
-#ifndef JM_BWD_KEEP_E
-#define JM_BWD_KEEP_E 1
-#endif
-#ifndef JM_BWD_PREFETCH_ZO
-#define JM_BWD_PREFETCH_ZO 1
-#endif
-constexpr int kSub = JM_BWD_SUB;       // tokens per recomputed sub-chunk
-constexpr int kBwdWavesPerSimd = JM_BWD_WAVES_PER_SIMD;   // the second __launch_bounds__ argument
+constexpr int kSub = 4;                // tokens per recomputed sub-chunk
+constexpr int kBwdWavesPerSimd = 4;    // the second __launch_bounds__ argument
 constexpr int kPiece = kBwdPiece;      // tokens per piece (a multiple of kSub)
 constexpr int kNSub = kPiece / kSub;
 static_assert(kPiece % kSub == 0, "pieces hold whole sub-chunks");
@@ -326,23 +314,17 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
   float dD = 0.0f;
   float pd[kSub], px[kSub];   // the next sub-chunk's per-channel inputs
   load2(nsub - 1, pd, px);
-#if JM_BWD_PREFETCH_ZO
   float pz[kSub], po[kSub];
   load2zo(nsub - 1, pz, po);
-#endif
   for (int k = nsub - 1; k >= 0; --k) {
     const int len = min(kSub, n_tok - k * kSub);
     float dv[kSub], xv[kSub], dyv[kSub], dzf[kSub];
-#if JM_BWD_PREFETCH_ZO
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
       dyv[j] = pz[j];
       dzf[j] = po[j];
     }
     load2zo(max(k - 1, 0), pz, po);
-#else
-    load2zo(k, dyv, dzf);
-#endif
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
       dv[j] = pd[j];
@@ -352,9 +334,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
     // recompute the sub-chunk's states: hist[j] = state after its token j, ehist[j] its decay factors; the
     // gate terms
     float hist[kSub][kQ];
-#if JM_BWD_KEEP_E
     float ehist[kSub][kQ];
-#endif
     const f32x4 c4 = ck[k][threadIdx.x];
     float hs[kQ];
 #pragma unroll
@@ -371,9 +351,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
 #pragma unroll
         for (int s = 0; s < kQ; ++s) {
           const float e = exp2_fast(d * a2[s]);
-#if JM_BWD_KEEP_E
           ehist[j][s] = e;
-#endif
           h[s] = fmaf(e, h[s], dx * Bv[s]);
           hist[j][s] = h[s];
         }
@@ -397,11 +375,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
 #pragma unroll
         for (int s = 0; s < kQ; ++s) {
           const float hp = j > 0 ? hist[j > 0 ? j - 1 : 0][s] : hs[s];
-#if JM_BWD_KEEP_E
           const float e = ehist[j][s];
-#else
-          const float e = exp2_fast(d * a2[s]);
-#endif
           const float g = fmaf(Cv[s], dy, u[s]);
           gB = fmaf(g, Bv[s], gB);
           const float ghe = g * hp * e;
