@@ -648,8 +648,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384,
-                    help="tokens of the headline workload the CPU oracle runs (a prefix; default 16384)")
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
+                    help="tokens of the headline workload the CPU oracle runs (a prefix; default 65536)")
     ap.add_argument("--config", type=int, default=3, choices=(1, 2, 3),
                     help="headline prefill workload: 3 = B1 L262144 (default), 1 = B1 L4096, 2 = B8 L4096")
     ap.add_argument("--no-other-prefills", action="store_true",
