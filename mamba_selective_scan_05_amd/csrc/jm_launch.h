@@ -109,6 +109,13 @@ int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes);
 void launch_skinny_gemm(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* R, int64_t ldr, void* Y,
                         int64_t ldy, int M, int N, int K, int splits, float* part, hipStream_t st);
 
+// fp32 contractions on the matrix cores: Y[m, n] = sum_k X[m, k] W[n, k] over `splits` equal K slices
+// (partial sums at Y + s * M * N), or with bias (splits = 1) softplus(. + bias[n]).  K / splits a multiple of
+// 4, X and W 16-byte aligned.  gemm_f32_tiles: the workgroups of one K slice.
+int64_t gemm_f32_tiles(int64_t M, int N);
+void launch_gemm_f32(const float* X, const float* W, const float* bias, float* Y, int M, int N, int K, int splits,
+                     hipStream_t st);
+
 // Scan pieces for B sequences of L tokens over C channels: about a fixed number of waves in the full pass,
 // pieces of at least 128 tokens, each piece's rows (row_bytes apart) under 2 GiB.
 void scan_plan(int B, int L, int C, int64_t row_bytes, int* P, int* Lp);

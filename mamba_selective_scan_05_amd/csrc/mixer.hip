@@ -116,6 +116,11 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
       p.narrow = true;
       grow(jm::xproj_column_groups(p.W, true));
     }
+  } else {
+    const int64_t tiles = jm::gemm_f32_tiles(p.T, p.W);
+    while (tiles * p.splits < kXprojWgTarget && p.splits * 2 <= jm::kMaxXprojSplits &&
+           (p.C / 64) % (p.splits * 2) == 0)
+      p.splits *= 2;
   }
 
   // scan pieces

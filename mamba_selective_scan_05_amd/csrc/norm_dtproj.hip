@@ -9,7 +9,8 @@
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation): for dt_rank <= 256 persistent 8-wave workgroups keep W_dt in
 // registers and stream 64-token dln tiles (dtproj_mfma_stream_kernel); larger ranks take a tiled kernel in
 // which a workgroup of 4 waves computes a 64-token x 256-channel tile and transposes it through LDS for
-// 16-byte stores.  Bias and softplus are fused into both epilogues.  fp32 path on the vector ALU.
+// 16-byte stores.  Bias and softplus are fused into both epilogues.  fp32 I/O: the fp32 matrix-core GEMM
+// (gemm_f32.hip) with the same epilogue.
 #include "jm_device.h"
 #include "jm_launch.h"
 
@@ -452,16 +453,6 @@ __global__ __launch_bounds__(64 * NW, 1) void dtproj_mfma_stream_kernel(const bf
   }
 }
 
-__global__ __launch_bounds__(256) void dtproj_f32_kernel(const float* __restrict__ dln, const float* __restrict__ w,
-                                                         const float* __restrict__ bias, float* __restrict__ delta,
-                                                         int M, int C, int R) {
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  const int m = blockIdx.x;   // tokens on the grid's x axis (the y and z axes hold at most 65536 workgroups)
-  if (c >= C) return;
-  float acc = 0.f;
-  for (int r = 0; r < R; ++r) acc = fmaf(dln[(int64_t)m * R + r], w[(int64_t)c * R + r], acc);
-  delta[(int64_t)m * C + c] = softplus(acc + bias[c]);
-}
 
 }  // namespace
 
@@ -501,9 +492,7 @@ void launch_dtproj(bool bf16, const void* dln, const void* w, const void* b, voi
                          (const bf16_t*)b, (bf16_t*)delta, M, C, R);
     }
   } else {
-    dim3 grid(M, (C + 255) / 256);
-    hipLaunchKernelGGL(dtproj_f32_kernel, grid, dim3(256), 0, st, (const float*)dln, (const float*)w,
-                       (const float*)b, (float*)delta, M, C, R);
+    launch_gemm_f32((const float*)dln, (const float*)w, (const float*)b, (float*)delta, M, C, R, 1, st);
   }
 }
 

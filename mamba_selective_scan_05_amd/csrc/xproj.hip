@@ -12,7 +12,8 @@
 // 8 XCDs round-robin, so each XCD works on a fixed subset of K slices and keeps their W_x rows in its own
 // L2.  Wider projections (N > 288) run as several column groups (grid z).
 //
-// fp32 path: plain fp32 dot products on the vector ALU (the fp32 I/O mode must not round xc to bf16).
+// fp32 path: the fp32 matrix-core GEMM of gemm_f32.hip (the fp32 I/O mode must not round xc to bf16), split
+// over channel slices like the bf16 path.
 #include "jm_device.h"
 #include "jm_launch.h"
 
@@ -270,24 +271,6 @@ __global__ __launch_bounds__(kThreads2) void xproj_mfma_tall_kernel(const bf16_t
   }
 }
 
-// fp32: one thread per (m, n); the xc row is staged through LDS in 1024-element pieces.
-__global__ __launch_bounds__(64) void xproj_f32_kernel(const float* __restrict__ xc, const float* __restrict__ w,
-                                                       float* __restrict__ part, int M, int N, int K) {
-  __shared__ float row[1024];
-  const int m = blockIdx.x;
-  const int n = blockIdx.y * 64 + threadIdx.x;
-  float acc = 0.0f;
-  for (int k0 = 0; k0 < K; k0 += 1024) {
-    const int kn = min(1024, K - k0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kn; i += 64) row[i] = xc[(int64_t)m * K + k0 + i];
-    __syncthreads();
-    if (n < N)
-      for (int i = 0; i < kn; ++i) acc = fmaf(row[i], w[(int64_t)n * K + k0 + i], acc);
-  }
-  if (n < N) part[(int64_t)m * N + n] = acc;
-}
-
 }  // namespace
 
 int xproj_token_tile(bool tall) { return tall ? kMT2 : kMT; }
@@ -315,8 +298,7 @@ void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, 
       hipLaunchKernelGGL(xproj_mfma_kernel<kNTWide>, grid, dim3(kThreads), 0, st, (const bf16_t*)xc,
                          (const bf16_t*)w, part, M, N, K, splits);
   } else {
-    dim3 grid(M, (N + 63) / 64);
-    hipLaunchKernelGGL(xproj_f32_kernel, grid, dim3(64), 0, st, (const float*)xc, (const float*)w, part, M, N, K);
+    launch_gemm_f32((const float*)xc, (const float*)w, nullptr, part, M, N, K, splits, st);
   }
 }
 
