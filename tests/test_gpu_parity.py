@@ -71,12 +71,12 @@ def test_ragged_multi_piece(io):
 
 
 def test_f32_jamba_widths_split_projections():
-    # fp32 I/O at d_inner 8192, dt_rank 256: x_proj's fp32 matrix-core GEMM splits its channels over 8
+    # fp32 I/O at d_inner 8192, dt_rank 256: x_proj's fp32 matrix-core GEMM splits its channels over 16
     # slices (8 token tiles x 5 column tiles), dt_proj's covers 8 x 128 tiles of 64 x 64 with a 32-wide K loop
     import mamba_selective_scan_05_amd as jm
     cfg = _small("f32_jamba_widths", 1, 512, 8192, 256, "f32", 31)
     w = make_weights(cfg, DEV)
-    assert jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen)).dbc_splits == 8
+    assert jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen)).dbc_splits == 16
     _run_and_check(cfg, w=w)
 
 
