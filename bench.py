@@ -34,12 +34,14 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
-# fp32 vector ALU: 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T lane-operations/s (AMD's published
-# 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops).  Transcendentals (exp, rcp) issue at a lower
-# rate: a throughput probe on the box measured 18.6 T/s for v_exp_f32 against 59.5 T/s for v_fma_f32, so
-# each counts as TRANS_SLOTS full-rate operations.
-VALU_PEAK_TOPS = 78.6
-TRANS_SLOTS = 3.2
+# fp32 vector ALU without packed math: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz = 39.3 T
+# lane-operations/s (a SIMD completes one wave64 fp32 instruction every 4 clocks; AMD's 157.3 TFLOP/s fp32
+# vector peak counts an FMA as two flops and a packed pair as two lanes: 39.3 x 2 x 2).  Transcendentals
+# (exp, rcp) issue at half that rate: a throughput probe on the box (32 independent chains per lane, 8 waves
+# per SIMD) took 4.6 nominal clocks per wave64 v_fma_f32 and 8.6 per v_exp_f32, so each counts as
+# TRANS_SLOTS full-rate operations.
+VALU_PEAK_TOPS = 39.3
+TRANS_SLOTS = 1.9
 N_STATE_SETS = 4               # decode state sets rotated per step (4 x 140 MB > the 256 MB last-level cache)
 
 
