@@ -10,8 +10,8 @@
 //
 // Layout: four lanes per channel, each holding four of its 16 states (lane 4c + q holds states 4q..4q+3), so
 // a workgroup of 256 lanes covers 64 channels.  Sums over a channel's states (y, d delta, d x) are quad DPP
-// reductions; the sums over channels of d B / d C are DPP row reductions (the four lanes of a row that hold
-// the same states), then a sum over the block's 16 rows in LDS, then over blocks in a reduce kernel.
+// reductions; the sums over channels of d B / d C take one DPP step over pairs of channels, then a sum over the
+// block's 32 pairs in LDS after each sub-chunk, then over blocks in a reduce kernel.
 //
 // Time is cut into pieces of kPiece tokens, as in the forward: the forward's local and carry passes give
 // every piece its incoming state; a backward local pass runs each piece's gradient recurrence from zero and
@@ -39,6 +39,7 @@ constexpr int kNSub = kPiece / kSub;
 static_assert(kPiece % kSub == 0, "pieces hold whole sub-chunks");
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+template <bool B> struct Flag { static constexpr bool value = B; };
 
 // v read from another lane of the same row (every lane valid for these controls); as a plain DPP move with
 // full masks the compiler folds it into the add that consumes it (v_add_f32 with a DPP source)
@@ -54,12 +55,11 @@ __device__ __forceinline__ float quad_sum(float v) {
   v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
   return v;
 }
-// sum over the four lanes of a 16-lane row holding the same state group (stride 4), in every lane
-__device__ __forceinline__ float row_q_sum(float v) {
+// lane r of a 16-lane row plus lane r + 4 (mod 16): the sum over a pair of channels of one state group; lanes
+// 0..3 and 8..11 of a row hold the sums of channel pairs (0, 1) and (2, 3)
+__device__ __forceinline__ float pair_sum(float v) {
 #pragma clang fp contract(off)
-  v += dpp<0x124>(v);  // row_ror:4
-  v += dpp<0x128>(v);  // row_ror:8
-  return v;
+  return v + dpp<0x124>(v);  // row_ror:4
 }
 
 struct Lane {
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   __shared__ f32x4 ck[kNSub][256];                 // state at each sub-chunk start, per lane
-  __shared__ f32x4 red[kSub][16][2 * kQ + 1];      // per-row d B / d C sums (4 x B, 4 x C float4, + pad)
+  __shared__ f32x4 red[kSub][32][2 * kQ];          // per channel pair: d B / d C sums (4 x B, 4 x C float4)
   __shared__ f32x4 sbc[kPiece][2 * kQ];            // B (4 x float4) then C (4 x float4) of each token
 
   for (int o = threadIdx.x; o < n_tok * 2 * kQ; o += 256)
@@ -316,8 +316,10 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
   load2(nsub - 1, pd, px);
   float pz[kSub], po[kSub];
   load2zo(nsub - 1, pz, po);
-  for (int k = nsub - 1; k >= 0; --k) {
-    const int len = min(kSub, n_tok - k * kSub);
+  // One sub-chunk of len tokens.  WHOLE (len == kSub: every sub-chunk but a ragged last one) drops the
+  // per-token conditions, which otherwise make the compiler shuffle registers between the paths.
+  auto sub_chunk = [&](auto whole, int k, int len) __attribute__((always_inline)) {
+    constexpr bool kWhole = decltype(whole)::value;
     float dv[kSub], xv[kSub], dyv[kSub], dzf[kSub];
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
     }
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
-      if (j < len) {
+      if (kWhole || j < len) {
         const f32x4 Bv = sbc[k * kSub + j][l.q];
         const float d = dv[j], x = xv[j];
         const float dx = d * x;
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
     // the gradient recurrence backwards through the sub-chunk
 #pragma unroll
     for (int j = kSub - 1; j >= 0; --j) {
-      if (j < len) {
+      if (kWhole || j < len) {
         const int i = k * kSub + j;
         const f32x4 Bv = sbc[i][l.q], Cv = sbc[i][kQ + l.q];
         const float d = dv[j], x = xv[j], dy = dyv[j];
@@ -395,20 +397,22 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
           gdz.st(i, fmaf(Dc, x, py) * dzf[j]);
         }
         dD = fmaf(dy, x, dD);
-        // d B / d C of this token summed over the row's four channels; lanes 0..3 of each row keep them
+        // d B / d C of this token summed over pairs of channels (one cross-lane step; the block's 32 pairs are
+        // added after the sub-chunk, from LDS)
 #pragma unroll
         for (int s = 0; s < kQ; ++s) {
-          vb[s] = row_q_sum(vb[s]);
-          vc[s] = row_q_sum(vc[s]);
+          vb[s] = pair_sum(vb[s]);
+          vc[s] = pair_sum(vc[s]);
         }
-        if ((lane & 15) < 4) {
-          red[j][wave * 4 + (lane >> 4)][l.q * 2] = f32x4{vb[0], vb[1], vb[2], vb[3]};
-          red[j][wave * 4 + (lane >> 4)][l.q * 2 + 1] = f32x4{vc[0], vc[1], vc[2], vc[3]};
+        if ((lane & 4) == 0) {
+          const int pr = wave * 8 + (lane >> 3);   // channel pair (lanes 0..3 and 8..11 of a row: pairs 2r, 2r + 1)
+          red[j][pr][l.q * 2] = f32x4{vb[0], vb[1], vb[2], vb[3]};
+          red[j][pr][l.q * 2 + 1] = f32x4{vc[0], vc[1], vc[2], vc[3]};
         }
       }
     }
     __syncthreads();
-    // sum the block's 16 rows and write this block's partial d B / d C for the sub-chunk's tokens
+    // sum the block's 32 channel pairs and write this block's partial d B / d C for the sub-chunk's tokens
     for (int o = threadIdx.x; o < len * 2 * kN; o += 256) {
       const int j = o / (2 * kN), col = o % (2 * kN);
       // column col: d B (col < N) or d C of state n = col % N, held by state group n / 4, element n % 4
@@ -416,10 +420,15 @@ __global__ __launch_bounds__(256, kBwdWavesPerSimd) void bwd_full_kernel(BwdArgs
       const float* base = reinterpret_cast<const float*>(&red[j][0][q * 2 + (col < kN ? 0 : 1)]) + n % kQ;
       float sum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += base[r * (2 * kQ + 1) * 4];
+      for (int r = 0; r < 32; ++r) sum += base[r * (2 * kQ) * 4];
       a.pbc[((int64_t)blockIdx.x * a.B * L + row0 + k * kSub + j) * (2 * kN) + col] = sum;
     }
     __syncthreads();
+  };
+  for (int k = nsub - 1; k >= 0; --k) {
+    const int len = min(kSub, n_tok - k * kSub);
+    if (len == kSub) sub_chunk(Flag<true>{}, k, len);
+    else sub_chunk(Flag<false>{}, k, len);
   }
 
   // per-piece partials of d A and d D, and d h0 from the first piece
