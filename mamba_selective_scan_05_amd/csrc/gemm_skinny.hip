@@ -6,10 +6,16 @@
 // of W (64 rows of the [N, K] weight) for every token, over a slice of K, and W's bytes are read from HBM
 // exactly once.  X (at most 256 x K, a few MB) is read by every workgroup and stays in the L2 caches.  Both
 // operands reach LDS through direct global-to-LDS loads in a three-stage pipeline with the swizzled
-// 128-byte rows of the x_proj kernel (16-byte chunk j of row r in slot j ^ (r & 7)).  Four waves each compute
-// 64 tokens x 64 columns.  When the column blocks alone leave the GPU short of workgroups (out_proj: 64 of
-// them) the K range is split and fp32 partial sums are added in split order by a second kernel, which also
-// adds the residual; the result does not depend on timing.
+// 128-byte rows of the x_proj kernel (16-byte chunk j of row r in slot j ^ (r & 7)).  Each wave computes
+// 64 tokens x 64 columns: four waves for a 64-column block, eight for a 128-column block.  When the column
+// blocks alone leave the GPU short of workgroups (out_proj: 64 of them) the K range is split and fp32 partial
+// sums are added in split order by a second kernel, which also adds the residual; the result does not depend
+// on timing.
+//
+// What bounds it is the rate at which L2 delivers X to the CUs (every workgroup re-reads X over its K slice:
+// for in_proj with 64-column blocks 512 MB of X against 134 MB of W).  With at least 128 blocks of 128
+// columns (in_proj at Jamba's widths) the workgroups take 128 columns over half the K range: half the X
+// re-reads, for 2 x M x N x 4 bytes of partial sums.
 #include "jm_device.h"
 #include "jm_launch.h"
 
@@ -23,11 +29,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_void_t;
 
 constexpr int kGM = 256;       // tokens per workgroup (the whole batch)
-constexpr int kGN = 64;        // output columns per workgroup
 constexpr int kGK = 64;        // K block staged in LDS
-constexpr int kGThreads = 256;
-constexpr int kGAL = kGM / 8 / 4;   // direct loads per wave per block: X rows / 8 per load / 4 waves
-constexpr int kGBL = kGN / 8 / 4;   // W rows / 8 / 4 waves
+constexpr int kGWideMin = 128; // 128-column blocks from this many of them on (two K slices: 256 workgroups)
 
 __device__ __forceinline__ int gswz(int r, int j) { return r * kGK + ((j ^ (r & 7)) << 3); }
 __device__ __forceinline__ bf16x8 gfrag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -41,20 +44,25 @@ __device__ __forceinline__ constexpr int gwait_vm(int n) {
   return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF);
 }
 
-// Workgroup w computes column block w / splits over K slice w % splits.  PARTIAL: fp32 partial sums to
-// part[s, m, n]; otherwise bf16(acc + R) to Y.
-template <bool PARTIAL>
-__global__ __launch_bounds__(kGThreads) void skinny_gemm_kernel(const bf16_t* __restrict__ X, int64_t ldx,
-                                                                const bf16_t* __restrict__ W, int64_t ldw,
-                                                                const bf16_t* R, int64_t ldr, bf16_t* Y,
-                                                                int64_t ldy, float* __restrict__ part, int M,
-                                                                int N, int K, int splits) {
+// Workgroup w computes column block w / splits (GN columns) over K slice w % splits.  PARTIAL: fp32 partial
+// sums to part[s, m, n]; otherwise bf16(acc + R) to Y.  Wave v: tokens 64 (v % 4) .., columns 64 (v / 4) ..
+template <bool PARTIAL, int GN>
+__global__ __launch_bounds__(GN * 4) void skinny_gemm_kernel(const bf16_t* __restrict__ X, int64_t ldx,
+                                                             const bf16_t* __restrict__ W, int64_t ldw,
+                                                             const bf16_t* R, int64_t ldr, bf16_t* Y,
+                                                             int64_t ldy, float* __restrict__ part, int M,
+                                                             int N, int K, int splits) {
+  constexpr int kWaves = GN / 16;
+  constexpr int kGAL = kGM / 8 / kWaves;   // direct loads per wave per block: X rows / 8 per load / waves
+  constexpr int kGBL = GN / 8 / kWaves;    // W rows / 8 / waves
+  static_assert(kGAL * 8 * kWaves == kGM && kGBL * 8 * kWaves == GN, "whole loads per wave");
   __shared__ __attribute__((aligned(16))) bf16_t As0[kGM * kGK], As1[kGM * kGK], As2[kGM * kGK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs0[kGN * kGK], Bs1[kGN * kGK], Bs2[kGN * kGK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs0[GN * kGK], Bs1[GN * kGK], Bs2[GN * kGK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;   // the wave's 64 tokens and 64 columns
   const int s = blockIdx.x % splits;
-  const int n0 = (blockIdx.x / splits) * kGN;
+  const int n0 = (blockIdx.x / splits) * GN;
   const int kps = K / splits;
   const int kbeg = s * kps;
   const int nblocks = kps / kGK;
@@ -103,9 +111,9 @@ __global__ __launch_bounds__(kGThreads) void skinny_gemm_kernel(const bf16_t* __
     for (int ks = 0; ks < kGK / 8; ks += 4) {
       bf16x8 a[4], bv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = gfrag(&A[gswz(wave * 64 + r * 16 + lr, ks + lk)]);
+      for (int r = 0; r < 4; ++r) a[r] = gfrag(&A[gswz(wm * 64 + r * 16 + lr, ks + lk)]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bv[t] = gfrag(&B[gswz(t * 16 + lr, ks + lk)]);
+      for (int t = 0; t < 4; ++t) bv[t] = gfrag(&B[gswz(wn * 64 + t * 16 + lr, ks + lk)]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -132,16 +140,17 @@ __global__ __launch_bounds__(kGThreads) void skinny_gemm_kernel(const bf16_t* __
   }
   __builtin_amdgcn_s_waitcnt(gwait_vm(0));   // the surplus loads land before the workgroup's LDS is reused
 
-  // accumulator (r, t) element i: token wave * 64 + r * 16 + (lane / 16) * 4 + i, column n0 + t * 16 + lane % 16
+  // accumulator (r, t) element i: token wm * 64 + r * 16 + (lane / 16) * 4 + i, column n0 + wn * 64 + t * 16 +
+  // lane % 16
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = wave * 64 + r * 16 + lk * 4 + i;
+      const int m = wm * 64 + r * 16 + lk * 4 + i;
       if (m >= M) continue;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int n = n0 + t * 16 + lr;
+        const int n = n0 + wn * 64 + t * 16 + lr;
         if (PARTIAL) {
           part[((int64_t)s * M + m) * N + n] = acc[r][t][i];
         } else {
@@ -190,12 +199,20 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
 
 }  // namespace
 
+// 128-column blocks when there are at least kGWideMin of them, else 64
+static int skinny_cols(int N) { return (N % 128 == 0 && N / 128 >= kGWideMin) ? 128 : 64; }
+
 int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes) {
-  if (M < 1 || M > kGM || N % kGN != 0 || K % kGK != 0) return 0;
+  if (M < 1 || M > kGM || N % 64 != 0 || K % kGK != 0) return 0;
+  // 128-column blocks over two K slices (half the X re-reads of 64-column blocks) when the slices and their
+  // partial sums fit; otherwise 64-column blocks, which then number at least 512 and need no split
+  if (skinny_cols(N) == 128 && (K / kGK) % 2 == 0 && K / kGK / 2 >= 4 && (int64_t)2 * M * N * 4 <= ws_bytes)
+    return 2;
+  const int gn = 64;
   int splits = 1;
   // split K until there are about as many workgroups as compute units, keeping every slice a whole number
   // of K blocks and the partial sums within the workspace
-  while ((int64_t)(N / kGN) * splits < 256 && (K / kGK) % (splits * 2) == 0 && K / kGK / (splits * 2) >= 4 &&
+  while ((int64_t)(N / gn) * splits < 256 && (K / kGK) % (splits * 2) == 0 && K / kGK / (splits * 2) >= 4 &&
          (int64_t)splits * 2 * M * N * 4 <= ws_bytes)
     splits *= 2;
   return splits;
@@ -203,14 +220,19 @@ int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes) {
 
 void launch_skinny_gemm(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* R, int64_t ldr, void* Y,
                         int64_t ldy, int M, int N, int K, int splits, float* part, hipStream_t st) {
-  dim3 grid((unsigned)((N / kGN) * splits));
-  if (splits == 1) {
-    hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, dim3(kGThreads), 0, st, (const bf16_t*)X, ldx,
+  const int gn = skinny_cols(N) == 128 && splits == 2 ? 128 : 64;   // as skinny_gemm_splits planned it
+  dim3 grid((unsigned)((N / gn) * splits));
+  if (gn == 128) {
+    hipLaunchKernelGGL((skinny_gemm_kernel<true, 128>), grid, dim3(512), 0, st, (const bf16_t*)X, ldx,
+                       (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, splits);
+  } else if (splits == 1) {
+    hipLaunchKernelGGL((skinny_gemm_kernel<false, 64>), grid, dim3(256), 0, st, (const bf16_t*)X, ldx,
                        (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, 1);
     return;
+  } else {
+    hipLaunchKernelGGL((skinny_gemm_kernel<true, 64>), grid, dim3(256), 0, st, (const bf16_t*)X, ldx,
+                       (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, splits);
   }
-  hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, dim3(kGThreads), 0, st, (const bf16_t*)X, ldx,
-                     (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, splits);
   const int64_t n = (int64_t)M * (N / 8);
   hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, splits, M,
                      N, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy);

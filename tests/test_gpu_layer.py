@@ -90,6 +90,14 @@ def test_layer_prefill_up_to_256_tokens_in_place(B, L):
     _check_prefill(cfg, True, in_place=True)
 
 
+def test_layer_prefill_wide_in_proj_blocks():
+    # d_inner 8192 makes in_proj 16384 columns wide: the weight-streaming kernel takes 128-column blocks over
+    # two K slices (partial sums added by the reduce kernel); 200 tokens leave a ragged last token group
+    cfg = MixerConfig("layer_skinny_wide", batch=2, seqlen=100, d_inner=8192, dt_rank=64, io_dtype="bf16", seed=36,
+                      d_model=512)
+    _check_prefill(cfg, True, in_place=True)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_layer_decode_steps(io):
     cfg = MixerConfig(f"layer_decode_{io}", batch=3, seqlen=1, d_inner=128, dt_rank=16, io_dtype=io, seed=33,
