@@ -80,6 +80,16 @@ def test_f32_jamba_widths_split_projections():
     _run_and_check(cfg, w=w)
 
 
+def test_f32_many_token_tiles():
+    # fp32 I/O over 2 x 4096 tokens: x_proj's fp32 GEMM runs 128 x 2 tiles over 4 channel slices, dt_proj's
+    # 128 x 16 tiles; the scan over several pieces per sequence
+    import mamba_selective_scan_05_amd as jm
+    cfg = _small("f32_many_tiles", 2, 4096, 1024, 64, "f32", 32)
+    w = make_weights(cfg, DEV)
+    assert jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen)).dbc_splits == 4
+    _run_and_check(cfg, w=w)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_largest_dt_rank(io):
     # dt_rank 512 (the largest supported): x_proj runs as two column groups and dt_proj takes its
