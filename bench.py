@@ -12,7 +12,8 @@ library's kernels (jm_mixer_prefill_profiled) for the per-kernel roofline: the s
 carry and full passes) against HBM with its fixed algorithmic bytes, its vector-ALU rate alongside.  The
 decode workload rotates its fp32 state over 4 sets so that it streams from HBM.  The whole Mamba layer
 around the mixer, the serving-style calls (a packed batch of prompts of mixed lengths, decode over a state
-pool), the exact-ZOH variant and the gated scan's training forward and backward are timed at the 4K shapes.
+pool), the exact-ZOH and fp32 I/O variants and the gated scan's training forward and backward are timed at the
+4K shapes.
 The fp64 CPU oracle is timed first, on the host's cores, on a prefix of the headline workload as a
 baseline.
 
@@ -657,7 +658,7 @@ def main():
     ap.add_argument("--no-other-prefills", action="store_true",
                     help="skip the prefill workloads other than the headline one")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
-    ap.add_argument("--no-variants", action="store_true", help="skip the ZOH-variant prefill timing")
+    ap.add_argument("--no-variants", action="store_true", help="skip the ZOH and fp32 variant prefill timings")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the gated scan's training forward / backward timing")
     ap.add_argument("--training-only", action="store_true",
@@ -788,6 +789,14 @@ def main():
             "scan_gate_us": round(zg["scan_gate"] * 1e3, 2)}}
         if pre1:
             result["variants"]["zoh_prefill"]["vs_default"] = round(pre1["ms_per_step"] / zp["ms"], 3)
+        # fp32 I/O (projections on the fp32 matrix cores, nothing rounded to bf16), on the 4K prefill
+        f32 = one.replace(io_dtype="f32")
+        log(f"prefill {one.name} with fp32 I/O: warmup {args.warmup}, steps {args.steps}")
+        fp = time_prefill(jm, f32, args.steps, args.warmup, hip)
+        result["variants"]["f32_prefill"] = {
+            "workload": f"{one.name} with fp32 x, z, weights and outputs",
+            "us_per_step": round(fp["ms"] * 1e3, 2), "tokens_per_s": round(ztok / (fp["ms"] * 1e-3), 1),
+            "stage_us": {k: round(v * 1e3, 2) for k, v in fp["stage_ms"].items()}}
     if not args.no_training:
         log(f"training (scan forward / backward): warmup {args.warmup}, steps {args.steps}")
         result["training"] = time_training(jm, args.steps, args.warmup)
