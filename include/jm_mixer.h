@@ -255,7 +255,7 @@ typedef struct jm_workspace_layout {
   int32_t scan_chunks;    /* number of sequence pieces the scan runs in parallel per channel */
   int64_t total_bytes;
   int32_t xproj_path;     /* x_proj kernel layout: 0: bf16 matrix cores, 128-token x 288-column tiles;
-                             1: bf16 matrix cores, 32-column groups (few tokens); 2: fp32 on the vector ALU;
+                             1: bf16 matrix cores, 32-column groups (few tokens); 2: fp32 on the matrix cores;
                              3: bf16 matrix cores, 256-token x 288-column tiles (32768 tokens or more) */
   int32_t reserved;
 } jm_workspace_layout;
