@@ -13,7 +13,7 @@ carry and full passes) against HBM with its fixed algorithmic bytes, its vector-
 decode workload rotates its fp32 state over 4 sets so that it streams from HBM.  The whole Mamba layer
 around the mixer, the serving-style calls (a packed batch of prompts of mixed lengths, decode over a state
 pool), the exact-ZOH and fp32 I/O variants and the gated scan's training forward and backward are timed at the
-4K shapes.
+4K shapes, and the decode step as one cooperative kernel beside the default decode step.
 The fp64 CPU oracle is timed first, on the host's cores, on a prefix of the headline workload as a
 baseline.
 
@@ -228,7 +228,7 @@ def time_prefill(jm, cfg, steps, warmup, hip, zoh=False):
             "step_pct": percentiles(per_step)}
 
 
-def time_decode(jm, cfg, steps, warmup, hip):
+def time_decode(jm, cfg, steps, warmup, hip, single=False):
     import torch
     from jm_inputs import make_state, make_weights
 
@@ -249,11 +249,16 @@ def time_decode(jm, cfg, steps, warmup, hip):
 
     def step(i):
         c, h = sets[i % N_STATE_SETS]
-        s = jm.call_decode_step(dims, m.packed, xs[i % 8].data_ptr(), zs[i % 8].data_ptr(), out.data_ptr(),
-                                c.data_ptr(), c.data_ptr(), h.data_ptr(), h.data_ptr(), ws.data_ptr(), ws.numel(),
-                                stream)
+        if single:
+            s = jm.call_decode_step_single_kernel(dims, m.packed, xs[i % 8].data_ptr(), zs[i % 8].data_ptr(),
+                                                  out.data_ptr(), c.data_ptr(), c.data_ptr(), h.data_ptr(),
+                                                  h.data_ptr(), 0, None, ws.data_ptr(), ws.numel(), stream)
+        else:
+            s = jm.call_decode_step(dims, m.packed, xs[i % 8].data_ptr(), zs[i % 8].data_ptr(), out.data_ptr(),
+                                    c.data_ptr(), c.data_ptr(), h.data_ptr(), h.data_ptr(), ws.data_ptr(),
+                                    ws.numel(), stream)
         if s != 0:
-            raise jm.JMError(s, "jm_mixer_decode_step")
+            raise jm.JMError(s, "jm_mixer_decode_step_single_kernel" if single else "jm_mixer_decode_step")
 
     for i in range(warmup):
         step(i)
@@ -265,6 +270,8 @@ def time_decode(jm, cfg, steps, warmup, hip):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    if single:
+        return {"ms": ms}
 
     nst = 7
     names = [jm.lib().jm_stage_name(i).decode() for i in range(nst)]
@@ -586,14 +593,18 @@ def run_decode(jm, dcfg, args, hip):
     dec = time_decode(jm, dcfg, args.steps, args.warmup, hip)
     db = decode_bytes(dcfg.batch, dcfg.d_inner, dcfg.d_state, dcfg.dt_rank, dcfg.d_conv, 2)
     gbs = db / (dec["ms"] * 1e-3) / 1e9
-    for k, t in dec["stage_ms"].items():
+    stages = dec["stage_ms"]
+    # the single-kernel step records every stage event after its one kernel: report it as one stage
+    if sum(v for k, v in stages.items() if k != "conv_silu") < 0.01 * dec["ms"]:
+        stages = {"decode_step_kernel": sum(stages.values())}
+    for k, t in stages.items():
         log(f"  {k:12s} {t * 1e3:9.2f} us")
     return {"workload": f"{dcfg.name}: one token per sequence, state rotated over {N_STATE_SETS} sets",
             "batch": dcfg.batch, "us_per_step": round(dec["ms"] * 1e3, 2),
             "tokens_per_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "alg_bytes": db,
             "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
             "step_us_events": dec["step_pct"],
-            "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()}}
+            "stage_us": {k: round(v * 1e3, 2) for k, v in stages.items()}}
 
 
 def run_prefill(jm, cfg, args, hip):
@@ -658,7 +669,8 @@ def main():
     ap.add_argument("--no-other-prefills", action="store_true",
                     help="skip the prefill workloads other than the headline one")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer timing")
-    ap.add_argument("--no-variants", action="store_true", help="skip the ZOH and fp32 variant prefill timings")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the variant timings (ZOH and fp32 prefill, single-kernel decode)")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the gated scan's training forward / backward timing")
     ap.add_argument("--training-only", action="store_true",
@@ -667,6 +679,8 @@ def main():
                     help="skip the serving-style timings (packed prefill, pooled-state decode)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workload and print its figures (for per-workload profiles)")
+    ap.add_argument("--single-kernel-decode", action="store_true",
+                    help="with --decode-only: also time jm_mixer_decode_step_single_kernel")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the headline prefill workload (for per-workload profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -705,7 +719,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.decode_only:
-        print(json.dumps({"decode": run_decode(jm, CONFIGS[4], args, hip)}), flush=True)
+        out = {"decode": run_decode(jm, CONFIGS[4], args, hip)}
+        if args.single_kernel_decode:
+            sk = time_decode(jm, CONFIGS[4], args.steps, args.warmup, hip, single=True)
+            out["decode_single_kernel_us_per_step"] = round(sk["ms"] * 1e3, 2)
+        print(json.dumps(out), flush=True)
         return
     if args.training_only:
         print(json.dumps({"training": time_training(jm, args.steps, args.warmup)}), flush=True)
@@ -797,6 +815,18 @@ def main():
             "workload": f"{one.name} with fp32 x, z, weights and outputs",
             "us_per_step": round(fp["ms"] * 1e3, 2), "tokens_per_s": round(ztok / (fp["ms"] * 1e-3), 1),
             "stage_us": {k: round(v * 1e3, 2) for k, v in fp["stage_ms"].items()}}
+        # the decode step as one cooperative kernel (jm_mixer_decode_step_single_kernel), beside the default
+        dcfg = CONFIGS[4]
+        log(f"decode {dcfg.name} as one kernel: warmup {args.warmup}, steps {args.steps}")
+        sk = time_decode(jm, dcfg, args.steps, args.warmup, hip, single=True)
+        db = decode_bytes(dcfg.batch, dcfg.d_inner, dcfg.d_state, dcfg.dt_rank, dcfg.d_conv, 2)
+        result["variants"]["decode_single_kernel"] = {
+            "workload": f"{dcfg.name}: jm_mixer_decode_step_single_kernel, state rotated over {N_STATE_SETS} sets",
+            "us_per_step": round(sk["ms"] * 1e3, 2), "tokens_per_s": round(dcfg.batch / (sk["ms"] * 1e-3), 1),
+            "frac_hbm": round(db / (sk["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if "decode" in result:
+            result["variants"]["decode_single_kernel"]["vs_default"] = round(
+                result["decode"]["us_per_step"] / (sk["ms"] * 1e3), 3)
     if not args.no_training:
         log(f"training (scan forward / backward): warmup {args.warmup}, steps {args.steps}")
         result["training"] = time_training(jm, args.steps, args.warmup)

@@ -141,7 +141,8 @@ int jm_mixer_prefill(const jm_mixer_dims* dims, const jm_mixer_weights* weights,
                      const float* ssm_state_in, float* ssm_state_out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace jm_mixer_decode_step needs for these dims (0 if invalid). */
+/* Bytes of device workspace jm_mixer_decode_step (and jm_mixer_decode_step_slots and
+ * jm_mixer_decode_step_single_kernel) needs for these dims (0 if invalid). */
 size_t jm_mixer_decode_workspace_size(const jm_mixer_dims* dims);
 
 /*
@@ -206,6 +207,32 @@ int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights
                                const void* x, const void* z, void* out,
                                void* conv_state_pool, float* ssm_state_pool, int32_t pool_size,
                                const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The decode step as a single kernel, the one-token step of the generation loop (TransformerLens
+ * "supported_architectures.jamba": generation carries the Mamba conv and recurrent caches from token to
+ * token): one cooperative launch with two grid-wide barriers — conv + SiLU and the x_proj partial sums per
+ * unit of 32 sequences x 256 channels, then the dt / B / C norms per sequence, then dt_proj, the state update
+ * and the gate per unit.
+ *   slots == NULL     jm_mixer_decode_step: the same arguments, layouts and aliasing (pool_size ignored).
+ *   slots != NULL     jm_mixer_decode_step_slots: conv_state_in / ssm_state_in are the pools of pool_size
+ *                     rows, updated in place (conv_state_out and ssm_state_out must equal them, else
+ *                     JM_ERR_INVALID_ARG); slot semantics as there.
+ *   workspace         at least jm_mixer_decode_workspace_size(dims) bytes, as for jm_mixer_decode_step; its
+ *                     contents on entry do not matter (the grid barriers key their flags to the launch).
+ * Results agree with jm_mixer_decode_step within the bf16 tolerance (its x_proj is summed over 256-channel
+ * slices instead).  Supported: bf16 I/O, d_inner a multiple of 256, dt_rank a multiple of 32 up to 256, at
+ * most 1024 sequences, on a device with cooperative launches; anything else returns JM_ERR_UNSUPPORTED with
+ * nothing enqueued (there is no fallback to the multi-kernel step).  On MI355X this is slower than
+ * jm_mixer_decode_step, which stays the default decode path: a cooperative launch costs ~20 us of dispatch,
+ * and each grid barrier ~5-7 us, more than the separate kernels' boundaries.
+ */
+int jm_mixer_decode_step_single_kernel(const jm_mixer_dims* dims, const jm_mixer_weights* weights,
+                                       const void* x, const void* z, void* out,
+                                       const void* conv_state_in, void* conv_state_out,
+                                       const float* ssm_state_in, float* ssm_state_out,
+                                       int32_t pool_size, const int32_t* slots,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace jm_mixer_prefill_varlen needs for these dims (0 if the dims are invalid). */
 size_t jm_mixer_prefill_varlen_workspace_size(const jm_mixer_dims* dims);

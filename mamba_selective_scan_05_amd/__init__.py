@@ -12,7 +12,7 @@ from ._lib import (JM_BF16, JM_DISC_EULER, JM_DISC_ZOH, JM_F32, JMError, Mixer, 
                    status_string, workspace_layout)
 from ._lib import Layer, LayerDims, LayerWeights, call_layer, layer_workspace_size, make_layer_dims  # noqa: F401
 from ._lib import call_decode_step_slots, call_prefill_varlen, varlen_workspace_size  # noqa: F401
-from ._lib import call_decode_step_noalloc, noalloc_scratch_limit  # noqa: F401
+from ._lib import call_decode_step_noalloc, call_decode_step_single_kernel, noalloc_scratch_limit  # noqa: F401
 from ._lib import decode_step, mixer_for, prefill  # noqa: F401
 from ._lib import (ScanDims, scan_backward, scan_dims, scan_forward, scan_saved_states_size,  # noqa: F401
                    scan_workspace_size)

@@ -107,6 +107,9 @@ def lib() -> ctypes.CDLL:
         L.jm_mixer_decode_noalloc_scratch_limit.restype = S
         L.jm_mixer_decode_step_slots.argtypes = [P(Dims), P(Weights), V, V, V, V, V, ctypes.c_int32, V, V, S, V]
         L.jm_mixer_decode_step_slots.restype = I
+        L.jm_mixer_decode_step_single_kernel.argtypes = [P(Dims), P(Weights), V, V, V, V, V, V, V, ctypes.c_int32, V,
+                                                         V, S, V]
+        L.jm_mixer_decode_step_single_kernel.restype = I
         L.jm_layer_decode_step_slots.argtypes = [P(LayerDims), P(LayerWeights), V, V, V, V, ctypes.c_int32, V, V,
                                                  S, V]
         L.jm_layer_decode_step_slots.restype = I
@@ -197,6 +200,13 @@ def call_decode_step_noalloc(dims: Dims, weights: Weights, x, z, out, conv_in, c
     """jm_mixer_decode_step_noalloc: the decode step with the library's own device scratch (no workspace)."""
     return lib().jm_mixer_decode_step_noalloc(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in, h_out,
                                               stream)
+
+
+def call_decode_step_single_kernel(dims: Dims, weights: Weights, x, z, out, conv_in, conv_out, h_in, h_out,
+                                   pool_size: int, slots, ws, ws_bytes: int, stream: int) -> int:
+    """jm_mixer_decode_step_single_kernel on integer device pointers (slots None: a plain batch)."""
+    return lib().jm_mixer_decode_step_single_kernel(_ref(dims), _ref(weights), x, z, out, conv_in, conv_out, h_in,
+                                                    h_out, pool_size, slots, ws, ws_bytes, stream)
 
 
 def noalloc_scratch_limit() -> int:
@@ -317,9 +327,10 @@ class Mixer:
 
     def decode_step(self, x: torch.Tensor, z: torch.Tensor, conv_state: torch.Tensor, ssm_state: torch.Tensor,
                     out: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None,
-                    ssm_state_out: Optional[torch.Tensor] = None, in_place: bool = False
-                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-        """One token per sequence: x, z are [B, C].  With in_place=True the states are updated in place."""
+                    ssm_state_out: Optional[torch.Tensor] = None, in_place: bool = False,
+                    single_kernel: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """One token per sequence: x, z are [B, C].  With in_place=True the states are updated in place;
+        single_kernel=True runs jm_mixer_decode_step_single_kernel instead of jm_mixer_decode_step."""
         B, C = x.shape
         dims = self.dims(B, 1, _row_stride(x, 1), _row_stride(z, 1))
         nbytes = decode_workspace_size(dims)
@@ -336,6 +347,13 @@ class Mixer:
             ssm_state_out = torch.empty_like(ssm_state)
         _check_contiguous(out=out, conv_state=conv_state, conv_state_out=conv_state_out, ssm_state=ssm_state,
                           ssm_state_out=ssm_state_out)
+        if single_kernel:
+            s = call_decode_step_single_kernel(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_state),
+                                               _ptr(conv_state_out), _ptr(ssm_state), _ptr(ssm_state_out), 0, None,
+                                               _ptr(ws), ws.numel(), _stream(self.device))
+            if s != JM_OK:
+                raise JMError(s, "jm_mixer_decode_step_single_kernel")
+            return out, conv_state_out, ssm_state_out
         s = call_decode_step(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_state), _ptr(conv_state_out),
                              _ptr(ssm_state), _ptr(ssm_state_out), _ptr(ws), ws.numel(), _stream(self.device))
         if s != JM_OK:
@@ -384,9 +402,11 @@ class Mixer:
         return out, conv_state_out, ssm_state_out
 
     def decode_step_slots(self, x: torch.Tensor, z: torch.Tensor, conv_pool: torch.Tensor, ssm_pool: torch.Tensor,
-                          slots: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                          slots: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          single_kernel: bool = False) -> torch.Tensor:
         """One token per sequence with the states in pools ([P, C, K-1] and [P, C, N]) updated in place at
-        rows slots[b] (a device int32 [B]; an entry outside [0, P) runs from zero states and stores none)."""
+        rows slots[b] (a device int32 [B]; an entry outside [0, P) runs from zero states and stores none).
+        single_kernel=True runs jm_mixer_decode_step_single_kernel instead of jm_mixer_decode_step_slots."""
         B, C = x.shape
         pool = _check_pools(conv_pool, ssm_pool, slots, B)
         dims = self.dims(B, 1, _row_stride(x, 1), _row_stride(z, 1))
@@ -397,6 +417,13 @@ class Mixer:
         if out is None:
             out = torch.empty((B, C), dtype=self.dtype, device=self.device)
         _check_contiguous(out=out)
+        if single_kernel:
+            s = call_decode_step_single_kernel(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_pool),
+                                               _ptr(conv_pool), _ptr(ssm_pool), _ptr(ssm_pool), pool, _ptr(slots),
+                                               _ptr(ws), ws.numel(), _stream(self.device))
+            if s != JM_OK:
+                raise JMError(s, "jm_mixer_decode_step_single_kernel")
+            return out
         s = call_decode_step_slots(dims, self.packed, _ptr(x), _ptr(z), _ptr(out), _ptr(conv_pool), _ptr(ssm_pool),
                                    pool, _ptr(slots), _ptr(ws), ws.numel(), _stream(self.device))
         if s != JM_OK:

@@ -17,7 +17,6 @@ namespace jm {
 
 namespace {
 
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kFT = 64;          // rows of X and of W per tile
 constexpr int kFK = 32;          // K block

@@ -7,6 +7,7 @@
 namespace jm {
 
 typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 // bf16 <-> fp32.  Widening is exact (the bf16 bits are the high half of the fp32); narrowing rounds to
 // nearest-even through the hardware converter (v_cvt_pk_bf16_f32 on gfx950).
@@ -95,6 +96,45 @@ __device__ __forceinline__ int64_t state_row(const int32_t* slots, int pool, int
   if (!slots) return s;
   const int r = slots[s];
   return r >= 0 && r < pool ? r : -1;
+}
+
+// A wave's 64 channels of a [rows, C, 16] fp32 state are 4 KB of contiguous memory.  They move between HBM
+// and registers through a 4 KB LDS tile, as four 1 KB rows of contiguous 16-byte lanes: per-lane 64-byte
+// strides would make each 16-byte access instruction touch 32 cache lines for 1 KB of data (this is the
+// whole traffic of a one-token step).  In LDS, chunk q of lane l sits in slot q ^ ((l >> 2) & 3) of the
+// lane's 64 bytes, which keeps the per-lane 16-byte reads and writes free of bank conflicts.  The HBM side
+// uses non-temporal loads and stores: a state is read once and written once per call, and keeping it out
+// of the caches leaves them to the weights and activations that are reused (the B = 256 decode step went
+// from 86 to 75 us with its four state sets rotated, i.e. with cold states).
+__device__ __forceinline__ int hslot(int l, int q) { return l * 16 + ((q ^ ((l >> 2) & 3)) << 2); }
+__device__ __forceinline__ void state_load(const float* src, float* hs, int lane, float* h) {
+  __builtin_amdgcn_wave_barrier();                    // the tile may still be in use by an earlier store
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = q * 64 + lane;                      // 16-byte chunk g of the wave's 4 KB
+    *reinterpret_cast<f32x4*>(&hs[hslot(g >> 2, g & 3)]) =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + g * 4));
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&hs[hslot(lane, q)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[q * 4 + i] = v[i];
+  }
+}
+__device__ __forceinline__ void state_store(float* dst, float* hs, int lane, const float* h) {
+  __builtin_amdgcn_wave_barrier();                    // the tile may still be in use by an earlier load
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(&hs[hslot(lane, q)]) = f32x4{h[q * 4], h[q * 4 + 1], h[q * 4 + 2], h[q * 4 + 3]};
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = q * 64 + lane;
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&hs[hslot(g >> 2, g & 3)]),
+                                 reinterpret_cast<f32x4*>(dst + g * 4));
+  }
 }
 
 }  // namespace jm

@@ -118,6 +118,51 @@ int64_t gemm_f32_tiles(int64_t M, int N);
 void launch_gemm_f32(const float* X, const float* W, const float* bias, float* Y, int M, int N, int K, int splits,
                      hipStream_t st);
 
+// The one-token step (bf16 I/O) as one cooperative kernel with two grid-wide barriers: conv + SiLU and the
+// x_proj partial sums per unit of 32 sequences x 256 channels, the norms per sequence, then dt_proj and the
+// state update per unit.  Plain batches and state pools (slots).
+// decode_fused_shape_ok: the shapes it takes (d_inner a multiple of 256, dt_rank a multiple of 32 up to 256,
+// at most 1024 sequences); decode_fused_available: the current device supports cooperative launches and
+// fits the kernel; decode_fused_slices: the x_proj slices it writes (part: slices * B * (R + 2 N) floats).
+// xc is written only when a unit cannot stay in LDS (more units than resident workgroups).  Returns the
+// launch status.
+struct DecodeArgs {
+  const void* x;
+  int64_t xs;
+  const void* z;
+  int64_t zs;
+  const void* conv_w;
+  const void* conv_b;
+  const void* conv_in;
+  void* conv_out;
+  const void* x_proj_w;
+  const void* dt_norm_w;
+  const void* b_norm_w;
+  const void* c_norm_w;
+  float eps;
+  const void* dt_proj_w;
+  const void* dt_proj_b;
+  const void* A_log;
+  const void* D;
+  const float* h0;
+  float* h_out;
+  void* out;
+  const int32_t* slots;
+  int pool;
+  void* xc;      // [B, C]
+  float* part;   // [C / 256, B, R + 2N]
+  void* dln;     // [B, R]
+  float* bc;     // [B, 2N]
+  uint64_t* flags;    // kDecodeMaxGroups flags of the grid barriers (any contents)
+  uint64_t launch;    // set by launch_decode_fused
+  int B, C, R, zoh;
+};
+constexpr int kDecodeMaxGroups = 1024;
+bool decode_fused_shape_ok(int B, int C, int R);
+bool decode_fused_available();
+int decode_fused_slices(int C);
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t st);
+
 // Scan pieces for B sequences of L tokens over C channels: about a fixed number of waves in the full pass,
 // pieces of at least 128 tokens, each piece's rows (row_bytes apart) under 2 GiB.
 void scan_plan(int B, int L, int C, int64_t row_bytes, int* P, int* Lp);

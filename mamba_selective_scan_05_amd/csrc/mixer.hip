@@ -47,14 +47,16 @@ struct Plan {
   int splits;    // x_proj channel slices
   bool narrow;   // x_proj in 32-column groups (few tokens)
   bool tall;     // x_proj in 256-token tiles (long inputs)
+  bool fused;    // a shape the single-kernel decode step takes (its x_proj slices size the partial sums)
   int P, Lp;     // scan pieces per sequence, tokens per piece
   int64_t xs, zs;
   int nseq;      // packed batches: number of sequences (the plan itself runs B = 1 over L = all tokens)
-  int64_t off_xc, off_dbc, off_dln, off_bc, off_delta, off_loc, off_cin, off_snap, total;
+  int64_t off_xc, off_dbc, off_dln, off_bc, off_delta, off_loc, off_cin, off_snap, off_bar, total;
 };
 
 // Optional parts of a call: per-stage events, a state pool (slots), a packed batch (cu_seqlens).
 struct Extras {
+  bool single = false;   // jm_mixer_decode_step_single_kernel
   void** events = nullptr;
   int n_events = 0;
   const int32_t* slots = nullptr;
@@ -84,8 +86,9 @@ int check_dims(const jm_mixer_dims* d, bool decode) {
   return JM_OK;
 }
 
-// varlen: a packed batch of d->batch sequences holding d->seqlen tokens in all, planned as one sequence
-Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
+// varlen: a packed batch of d->batch sequences holding d->seqlen tokens in all, planned as one sequence.
+// single: the layout of jm_mixer_decode_step_single_kernel (its partial sums and grid-barrier flags).
+Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false, bool single = false) {
   Plan p;
   p.nseq = d->batch;
   p.B = varlen ? 1 : d->batch;
@@ -126,13 +129,17 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
       p.splits *= 2;
   }
 
+  p.fused = single && p.bf16 && p.L == 1 && !varlen && jm::decode_fused_shape_ok(p.B, p.C, p.R);
+  const int64_t dbc_slices =
+      p.fused && jm::decode_fused_slices(p.C) > p.splits ? jm::decode_fused_slices(p.C) : p.splits;
+
   // scan pieces
   const int64_t row_bytes = (p.xs > p.zs ? (p.xs > p.C ? p.xs : p.C) : (p.zs > p.C ? p.zs : p.C)) * p.esize;
   jm::scan_plan(p.B, p.L, p.C, row_bytes, &p.P, &p.Lp);
 
   int64_t off = 0;
   p.off_xc = off;    off += align_up(p.T * p.C * p.esize);
-  p.off_dbc = off;   off += align_up((int64_t)p.splits * p.T * p.W * 4);
+  p.off_dbc = off;   off += align_up(dbc_slices * p.T * p.W * 4);
   p.off_dln = off;   off += align_up(p.T * p.R * p.esize);
   p.off_bc = off;    off += align_up(p.T * 2 * p.N * 4);
   p.off_delta = off; off += align_up(p.T * p.C * p.esize);
@@ -143,6 +150,10 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false) {
     if (varlen) {
       p.off_snap = off; off += align_up((int64_t)p.P * p.N * p.C * 4);
     }
+  }
+  p.off_bar = -1;
+  if (p.fused) {
+    p.off_bar = off; off += align_up(jm::kDecodeMaxGroups * 8);
   }
   p.total = off > 0 ? off : kAlign;
   return p;
@@ -177,11 +188,12 @@ struct StageMarks {
 // Every check of a call, before anything is enqueued.
 int validate(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, const void* z, void* out,
              const void* conv_in, void* conv_out, const float* h0, float* h_out, void* ws, size_t ws_bytes,
-             bool decode, const int32_t* slots = nullptr, int pool = 0, const int32_t* cu = nullptr) {
+             bool decode, const int32_t* slots = nullptr, int pool = 0, const int32_t* cu = nullptr,
+             bool single = false) {
   int s = check_dims(dims, decode);
   if (s != JM_OK) return s;
   if ((s = check_weights(w)) != JM_OK) return s;
-  const Plan p = make_plan(dims, decode, cu != nullptr);
+  const Plan p = make_plan(dims, decode, cu != nullptr, single);
   if (!conv_out || !h_out) return JM_ERR_INVALID_ARG;
   if (decode && (!conv_in || !h0)) return JM_ERR_INVALID_ARG;
   if (slots) {   // a state pool: decode or packed prefill, at least one row, int32 indices
@@ -205,9 +217,10 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   const int32_t* slots = ex.slots;
   const int pool = ex.pool;
   const bool varlen = ex.cu != nullptr;
-  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool, ex.cu);
+  int s = validate(dims, w, x, z, out, conv_in, conv_out, h0, h_out, ws, ws_bytes, decode, slots, pool, ex.cu,
+                   ex.single);
   if (s != JM_OK) return s;
-  const Plan p = make_plan(dims, decode, varlen);
+  const Plan p = make_plan(dims, decode, varlen, ex.single);
   const jm::VarSeqs vs{ex.cu, slots, p.nseq, pool};
   if (events) {
     if (n_events < JM_STAGES + 1) return JM_ERR_INVALID_ARG;
@@ -234,9 +247,49 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
   float* bc = (float*)(base + p.off_bc);
   void* delta = base + p.off_delta;
 
-  marks.mark(0);
   // one token per sequence: the single-step conv also writes the conv state, so the scan skips it
   const bool step = p.L == 1 && !varlen;
+  if (ex.single) {
+    // the whole step as one kernel; nothing is enqueued for a shape or device it does not support
+    if (!step || !p.fused || !jm::decode_fused_available()) return JM_ERR_UNSUPPORTED;
+    marks.mark(0);
+    jm::DecodeArgs d;
+    d.x = x;
+    d.xs = p.xs;
+    d.z = z;
+    d.zs = p.zs;
+    d.conv_w = w->conv_w;
+    d.conv_b = w->conv_b;
+    d.conv_in = conv_in;
+    d.conv_out = conv_out;
+    d.x_proj_w = w->x_proj_w;
+    d.dt_norm_w = w->dt_norm_w;
+    d.b_norm_w = w->b_norm_w;
+    d.c_norm_w = w->c_norm_w;
+    d.eps = dims->norm_eps;
+    d.dt_proj_w = w->dt_proj_w;
+    d.dt_proj_b = w->dt_proj_b;
+    d.A_log = w->A_log;
+    d.D = w->D;
+    d.h0 = h0;
+    d.h_out = h_out;
+    d.out = out;
+    d.slots = slots;
+    d.pool = pool;
+    d.xc = xc;
+    d.part = dbc;
+    d.dln = dln;
+    d.bc = bc;
+    d.flags = (uint64_t*)(base + p.off_bar);
+    d.B = p.B;
+    d.C = p.C;
+    d.R = p.R;
+    d.zoh = dims->discretization == JM_DISC_ZOH;
+    const hipError_t e = jm::launch_decode_fused(d, st);
+    for (int i = 1; i <= JM_STAGES; ++i) marks.mark(i);
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
+  }
+  marks.mark(0);
   if (step) {
     jm::launch_conv_step(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, conv_out, p.B, p.C, st, slots,
                          pool);
@@ -356,7 +409,9 @@ size_t jm_mixer_prefill_workspace_size(const jm_mixer_dims* dims) {
 
 size_t jm_mixer_decode_workspace_size(const jm_mixer_dims* dims) {
   if (check_dims(dims, true) != JM_OK) return 0;
-  return (size_t)make_plan(dims, true).total;
+  // also room for jm_mixer_decode_step_single_kernel (its own layout for the shapes it takes)
+  const int64_t plain = make_plan(dims, true).total, single = make_plan(dims, true, false, true).total;
+  return (size_t)(plain > single ? plain : single);
 }
 
 int jm_mixer_prefill(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x, const void* z,
@@ -398,6 +453,21 @@ int jm_mixer_decode_step_slots(const jm_mixer_dims* dims, const jm_mixer_weights
   ex.pool = pool_size;
   return run(dims, weights, x, z, out, conv_state_pool, conv_state_pool, ssm_state_pool, ssm_state_pool,
              workspace, workspace_bytes, stream, true, ex);
+}
+
+int jm_mixer_decode_step_single_kernel(const jm_mixer_dims* dims, const jm_mixer_weights* weights, const void* x,
+                                       const void* z, void* out, const void* conv_state_in, void* conv_state_out,
+                                       const float* ssm_state_in, float* ssm_state_out, int32_t pool_size,
+                                       const int32_t* slots, void* workspace, size_t workspace_bytes, void* stream) {
+  Extras ex;
+  ex.single = true;
+  if (slots) {   // pools, updated in place
+    if (conv_state_out != conv_state_in || ssm_state_out != ssm_state_in) return JM_ERR_INVALID_ARG;
+    ex.slots = slots;
+    ex.pool = pool_size;
+  }
+  return run(dims, weights, x, z, out, conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, workspace,
+             workspace_bytes, stream, true, ex);
 }
 
 size_t jm_mixer_prefill_varlen_workspace_size(const jm_mixer_dims* dims) {

@@ -19,7 +19,6 @@ namespace jm {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 // norm: WPT waves per token (1, or 4 when there are few tokens), each summing S / WPT of the x_proj slices.
 // S (the number of slices) and COLS (columns per lane, 64 columns apart) are compile-time so that every

@@ -77,46 +77,6 @@ __device__ __forceinline__ void load_a2(const T* A_log, int c, float* a2) {
   for (int n = 0; n < kN; ++n) a2[n] = -exp2_fast(io<T>::ld(A_log + (int64_t)c * kN + n) * kLog2e) * kLog2e;
 }
 
-// The wave's 64 channels of a [B, C, 16] fp32 state are 4 KB of contiguous memory.  They move between HBM
-// and registers through a 4 KB LDS tile, as four 1 KB rows of contiguous 16-byte lanes: per-lane 64-byte
-// strides would make each 16-byte access instruction touch 32 cache lines for 1 KB of data (this is the
-// whole traffic of a one-token step).  In LDS, chunk q of lane l sits in slot q ^ ((l >> 2) & 3) of the
-// lane's 64 bytes, which keeps the per-lane 16-byte reads and writes free of bank conflicts.  The HBM side
-// uses non-temporal loads and stores: a state is read once and written once per call, and keeping it out
-// of the caches leaves them to the weights and activations that are reused (the B = 256 decode step went
-// from 86 to 75 us with its four state sets rotated, i.e. with cold states).
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-__device__ __forceinline__ int hslot(int l, int q) { return l * 16 + ((q ^ ((l >> 2) & 3)) << 2); }
-__device__ __forceinline__ void state_load(const float* src, float* hs, int lane, float* h) {
-  __builtin_amdgcn_wave_barrier();                    // the tile may still be in use by an earlier store
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int g = q * 64 + lane;                      // 16-byte chunk g of the wave's 4 KB
-    *reinterpret_cast<f32x4*>(&hs[hslot(g >> 2, g & 3)]) =
-        __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + g * 4));
-  }
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&hs[hslot(lane, q)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[q * 4 + i] = v[i];
-  }
-}
-__device__ __forceinline__ void state_store(float* dst, float* hs, int lane, const float* h) {
-  __builtin_amdgcn_wave_barrier();                    // the tile may still be in use by an earlier load
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<f32x4*>(&hs[hslot(lane, q)]) = f32x4{h[q * 4], h[q * 4 + 1], h[q * 4 + 2], h[q * 4 + 3]};
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int g = q * 64 + lane;
-    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&hs[hslot(g >> 2, g & 3)]),
-                                 reinterpret_cast<f32x4*>(dst + g * 4));
-  }
-}
-
 // FULL = false: the local pass (end state + delta sum of a piece); FULL = true: the output pass.
 // VAR: one packed axis of several sequences (a.cu).  A piece is walked as segments that each lie in one
 // sequence; at a sequence start the state is reset to that sequence's initial state, and the local pass

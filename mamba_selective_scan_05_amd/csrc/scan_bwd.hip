@@ -38,7 +38,6 @@ constexpr int kPiece = kBwdPiece;      // tokens per piece (a multiple of kSub)
 constexpr int kNSub = kPiece / kSub;
 static_assert(kPiece % kSub == 0, "pieces hold whole sub-chunks");
 
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 template <bool B> struct Flag { static constexpr bool value = B; };
 
 // v read from another lane of the same row (every lane valid for these controls); as a plain DPP move with

@@ -22,7 +22,6 @@ namespace jm {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kMT = 128;         // tokens per workgroup tile
 constexpr int kKB = 64;           // K block staged in LDS (one 128-byte LDS row per token / column)

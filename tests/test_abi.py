@@ -106,9 +106,13 @@ def test_workspace_sizes_and_layout():
     assert n >= T * C * 2 * 2 + lay.dbc_splits * T * W * 4 + T * 256 * 2 + T * 32 * 4
     offs = sorted([lay.xc, lay.dbc, lay.dln, lay.bc, lay.delta])
     assert offs[0] == 0 and all(o % 256 == 0 for o in offs) and offs[-1] < n
-    # decode needs a workspace sized for one token per sequence, independent of seqlen
+    # decode needs a workspace sized for one token per sequence, independent of seqlen, with room for the
+    # single-kernel step's wider x_proj partial sums (32 slices of 256 channels)
     dd = jm.make_dims(256, 9999, 8192, 256, jm.JM_BF16)
-    assert jm.decode_workspace_size(dd) == jm.prefill_workspace_size(jm.make_dims(256, 1, 8192, 256, jm.JM_BF16))
+    d1 = jm.make_dims(256, 1, 8192, 256, jm.JM_BF16)
+    assert jm.decode_workspace_size(dd) == jm.decode_workspace_size(d1)
+    assert jm.decode_workspace_size(d1) >= jm.prefill_workspace_size(d1)
+    assert jm.decode_workspace_size(d1) >= 32 * 256 * 288 * 4 + 256 * 8192 * 2
     with pytest.raises(jm.JMError):
         jm.workspace_layout(_dims(d_state=4))
 
@@ -276,3 +280,24 @@ def test_noalloc_decode_rejects_calls_beyond_its_scratch_before_launch():
     assert "32 MiB" in jm.status_string(_lib.JM_ERR_SCRATCH_LIMIT)
     # dims errors come first, as in jm_mixer_decode_step
     assert jm.call_decode_step_noalloc(_dims(d_state=8), _weights(), *args) == _lib.JM_ERR_UNSUPPORTED
+
+
+def test_single_kernel_decode_checks_before_launch():
+    # shapes and devices the single-kernel step does not take are refused with nothing enqueued (no fallback)
+    w = _weights()
+    args = lambda d, pool=0, slots=None, conv_out=FAKE, h_out=FAKE, ws_bytes=WS_BIG: (
+        d, w, FAKE, FAKE, FAKE, FAKE, conv_out, FAKE, h_out, pool, slots, FAKE, ws_bytes, 0)
+    f32 = _dims(batch=4, seqlen=1, d_inner=256, dt_rank=32, io_dtype=jm.JM_F32)
+    assert jm.call_decode_step_single_kernel(*args(f32)) == _lib.JM_ERR_UNSUPPORTED
+    narrow = _dims(batch=4, seqlen=1, d_inner=192, dt_rank=32, io_dtype=jm.JM_BF16)
+    assert jm.call_decode_step_single_kernel(*args(narrow)) == _lib.JM_ERR_UNSUPPORTED
+    rank8 = _dims(batch=4, seqlen=1, d_inner=256, dt_rank=8, io_dtype=jm.JM_BF16)
+    assert jm.call_decode_step_single_kernel(*args(rank8)) == _lib.JM_ERR_UNSUPPORTED
+    many = _dims(batch=1025, seqlen=1, d_inner=256, dt_rank=32, io_dtype=jm.JM_BF16)
+    assert jm.call_decode_step_single_kernel(*args(many)) == _lib.JM_ERR_UNSUPPORTED
+    ok = _dims(batch=4, seqlen=1, d_inner=256, dt_rank=32, io_dtype=jm.JM_BF16)
+    # argument errors come first: pools must be updated in place, the workspace must be large enough
+    assert jm.call_decode_step_single_kernel(*args(ok, pool=4, slots=FAKE, conv_out=FAKE + 256)) == \
+        _lib.JM_ERR_INVALID_ARG
+    assert jm.call_decode_step_single_kernel(*args(ok, ws_bytes=16)) == _lib.JM_ERR_WORKSPACE
+    assert jm.call_decode_step_single_kernel(*args(_dims(d_state=8))) == _lib.JM_ERR_UNSUPPORTED
