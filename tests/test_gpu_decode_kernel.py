@@ -6,8 +6,9 @@ grid-wide barrier, the norms per sequence, a second barrier, then dt_proj and th
 cases cover ragged last units (B not a multiple of 32), channel slice counts that are and are not a multiple
 of 8 (the two unit-to-workgroup mappings), more units than resident workgroups (units loop, xc through HBM),
 more sequences than workgroups (the norm phase loops), the exact zero-order hold, strided x / z, a state pool
-with slots outside it, repeated calls through one workspace (the barrier flags are keyed to each launch), and
-the Jamba decode shape against the default (multi-kernel) decode step.
+with slots outside it, repeated calls through one workspace (the barrier flags are keyed to each launch), a
+workspace poisoned with all bits set (determinism: two runs bit for bit), and the Jamba decode shape against
+the default (multi-kernel) decode step.
 """
 
 import pytest
@@ -135,3 +136,28 @@ def test_single_kernel_step_over_a_pool():
     assert_bitwise("conv pool (touched rows)", conv_pool[idx], torch.from_numpy(rc[touched]).to(pcfg.torch_dtype))
     r_ = torch.as_tensor(rest, device=DEV)
     assert torch.equal(conv_pool[r_], st["conv_state"][r_]) and torch.equal(ssm_pool[r_], st["ssm_state"][r_])
+
+
+def test_single_kernel_step_deterministic_over_a_poisoned_workspace():
+    # the grid barriers' flags live in the workspace: whatever it holds (here all bits set) must not let a
+    # workgroup pass early, and two runs must agree bit for bit
+    import mamba_selective_scan_05_amd as jm
+    cfg = MixerConfig("dk_poison", batch=96, seqlen=1, d_inner=2048, dt_rank=128, io_dtype="bf16", seed=335,
+                      with_state=True)
+    w = make_weights(cfg, DEV)
+    a = make_activations(cfg, DEV)
+    st = make_state(cfg, DEV)
+    m = jm.Mixer(w, cfg.dt_rank, cfg.d_state, cfg.d_conv, cfg.norm_eps)
+    x, z = a["x"][:, 0], a["z"][:, 0]
+    ws = m.workspace(jm.decode_workspace_size(m.dims(cfg.batch, 1)))
+    runs = []
+    for _ in range(2):
+        ws.fill_(0xFF)
+        runs.append(m.decode_step(x, z, st["conv_state"], st["ssm_state"], single_kernel=True))
+        torch.cuda.synchronize()
+    for i, name in enumerate(("out", "conv_state", "ssm_state")):
+        assert torch.isfinite(runs[0][i].float()).all(), name
+        assert torch.equal(runs[0][i], runs[1][i]), name
+    ro, rc, rh = oracle.mixer_decode_step(to_f64(x), to_f64(z), weights_f64(w), cfg.dt_rank, cfg.d_state,
+                                          to_f64(st["conv_state"]), to_f64(st["ssm_state"]), cfg.norm_eps)
+    assert_close("out", runs[1][0], ro, "bf16")
