@@ -5,16 +5,18 @@
 // caches from step to step; the arithmetic is the Jamba Guide's "Inside the Mamba State-Space Layers" with one
 // token).  Its only dependence across channels is x_proj, a contraction over all of them, followed by the
 // RMSNorms of its output rows; everything else is independent per (sequence, channel).  So one cooperative
-// launch (every workgroup resident at once, one 8-wave workgroup per CU) runs three phases separated by two grid-wide barriers:
+// launch (every workgroup resident at once, one 8-wave workgroup per CU) runs three phases separated by two
+// grid-wide barriers:
 //   1  per unit of 32 sequences x 256 channels: conv + bias + SiLU and the shifted conv state, then the unit's
 //      x_proj partial sums over its 256 channels on the matrix cores (v_mfma_f32_16x16x32_bf16);
 //   2  per sequence: the partial sums added in slice order, then the dt / B / C RMSNorms;
 //   3  per unit: dt_proj + bias + softplus on the matrix cores into LDS, then the state update, the D skip
 //      and the SiLU(z) gate; the unit's states stream through HBM as 4 KB rows (a wave's 64 channels of one
-//      sequence), two sequences' rows in flight per wave.
+//      sequence), three sequences' rows in flight per wave (one with the exact hold, for registers).
 // Between the phases nothing goes back to the host, and with one unit per workgroup the unit's xc stays in
-// LDS from phase 1 to phase 3.  The arithmetic of each step is that of the separate kernels (conv_silu.hip,
-// norm_dtproj.hip, scan.hip); only the x_proj slices differ (256 channels each here).
+// LDS from phase 1 to phase 3.  Each step computes what the separate kernels do (conv_silu.hip,
+// norm_dtproj.hip, scan.hip) up to summation order (x_proj slices of 256 channels here, the norms' sums of
+// squares reduced across waves) and, for the exact hold, A and 1 / A derived from A log2(e).
 //
 // Barrier: one flag per workgroup in the workspace, set to a token unique to the launch and the barrier (see
 // grid_barrier), so nothing needs zeroing between calls.  Every workgroup reaches both barriers (none returns
@@ -161,8 +163,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(DecodeArgs a) 
     }
     if (tid < kUT) srow[tid] = b0 + tid < B ? (int)state_row(a.slots, a.pool, b0 + tid) : -1;
     __syncthreads();                      // the previous unit's fragment reads of xs are done; srow is set
-    // item -> (row r of the unit, 8 channels g): 32 rows x 32 groups.  Rows past B recompute the last
-    // sequence and store nothing but their (unused) LDS row.
+    // item -> (row r of the unit, 8 channels g): 32 rows x 32 groups.  Rows past B read the last sequence's
+    // input with a zero state (their srow is -1) and store nothing but their (unused) LDS row.
     for (int it = tid; it < kUT * (kUC / 8); it += kThreads) {
       const int r = it >> 5, g = it & 31;
       const int bb = b0 + r, b = min(bb, B - 1);
