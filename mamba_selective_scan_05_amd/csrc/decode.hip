@@ -21,7 +21,8 @@
 // Barrier: one flag per workgroup in the workspace, set to a token unique to the launch and the barrier (see
 // grid_barrier), so nothing needs zeroing between calls.  Every workgroup reaches both barriers (none returns
 // early); the runtime refuses a cooperative launch that would not have every workgroup resident; and each
-// wait gives up after a bounded number of polls, so the kernel always ends.
+// wait gives up after a bounded number of polls (about a second), so the kernel always ends — with undefined
+// results if a wait ever gave up, which a cooperative launch rules out.
 #include <atomic>
 #include <chrono>
 #include <mutex>
