@@ -32,9 +32,9 @@ constexpr int64_t kScanWaveTarget = 6144;
 constexpr int kMinPiece = 128;
 // x_proj: split the contraction over channel slices until there are this many workgroups (one per CU).
 constexpr int kXprojWgTarget = 256;
-// fp32 x_proj (64 x 64 tiles, one wave per SIMD each, four resident per CU): split until there are four
-// workgroups per CU, so that every CU gets the same number of equal K slices.
-constexpr int kXprojF32WgTarget = 1024;
+// fp32 x_proj (128 x 96 tiles of 4 waves, two resident per CU): split until there are two workgroups per CU,
+// so that every CU gets the same number of equal K slices.
+constexpr int kXprojF32WgTarget = 512;
 // x_proj takes 256-token tiles from this many tokens on (fewer re-reads of W_x; shorter inputs keep 128-token
 // tiles, which need half as many channel slices and partial sums to fill the GPU).
 constexpr int64_t kXprojTallTokens = 32768;

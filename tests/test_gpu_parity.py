@@ -72,7 +72,8 @@ def test_ragged_multi_piece(io):
 
 def test_f32_jamba_widths_split_projections():
     # fp32 I/O at d_inner 8192, dt_rank 256: x_proj's fp32 matrix-core GEMM splits its channels over 16
-    # slices (8 token tiles x 5 column tiles), dt_proj's covers 8 x 128 tiles of 64 x 64 with a 32-wide K loop
+    # slices (4 token tiles x 3 column tiles of 128 x 96), dt_proj's covers 4 x 64 tiles of 128 x 128 with a
+    # 32-wide K loop
     import mamba_selective_scan_05_amd as jm
     cfg = _small("f32_jamba_widths", 1, 512, 8192, 256, "f32", 31)
     w = make_weights(cfg, DEV)
@@ -81,12 +82,12 @@ def test_f32_jamba_widths_split_projections():
 
 
 def test_f32_many_token_tiles():
-    # fp32 I/O over 2 x 4096 tokens: x_proj's fp32 GEMM runs 128 x 2 tiles over 4 channel slices, dt_proj's
-    # 128 x 16 tiles; the scan over several pieces per sequence
+    # fp32 I/O over 2 x 4096 tokens: x_proj's fp32 GEMM runs 64 token tiles (its 96 columns one tile) over 8
+    # channel slices, dt_proj's 64 x 8 tiles; the scan over several pieces per sequence
     import mamba_selective_scan_05_amd as jm
     cfg = _small("f32_many_tiles", 2, 4096, 1024, 64, "f32", 32)
     w = make_weights(cfg, DEV)
-    assert jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen)).dbc_splits == 4
+    assert jm.workspace_layout(_mixer(cfg, w).dims(cfg.batch, cfg.seqlen)).dbc_splits == 8
     _run_and_check(cfg, w=w)
 
 
