@@ -82,13 +82,16 @@ class Hip:
 
 def algorithmic_bytes(B, L, C, N, R, esize):
     """Fixed per-stage byte counts (what each step must move at minimum, in the I/O precision):
-    conv: x in, xc out; x_proj: xc in, dbc out (fp32), W_x once; norm + dt_proj: dbc in, delta out,
+    conv: x in, xc out; x_proj: xc in, dbc out (fp32), W_x once (conv + x_proj as one kernel: x in, xc and dbc
+    out, the weights once); norm + dt_proj: dbc in, delta out,
     B/C out (fp32), W_dt once; scan + gate: xc, delta, z in, B/C in, out, SSM state in and out (fp32)."""
     T = B * L
     W = R + 2 * N
     return {
         "conv_silu": T * C * 2 * esize + C * 5 * esize,
         "x_proj": T * C * esize + T * W * 4 + W * C * esize,
+        # the two as one kernel (long inputs): x in, xc out, dbc out, the weights once
+        "conv_silu_x_proj": T * C * 2 * esize + C * 5 * esize + T * W * 4 + W * C * esize,
         "norm_dt_proj": T * W * 4 + T * C * esize + T * 2 * N * 4 + C * R * esize + C * esize,
         "scan_gate": T * C * 4 * esize + T * 2 * N * 4 + 2 * B * C * N * 4 + C * (N + 1) * esize,
     }
@@ -153,10 +156,13 @@ def percentiles(vals_ms):
     return {"p10": round(pick(0.1) * 1e3, 2), "p50": round(pick(0.5) * 1e3, 2), "p90": round(pick(0.9) * 1e3, 2)}
 
 
-def stage_groups(stage_ms):
+def stage_groups(stage_ms, conv_in_xproj=False):
+    if conv_in_xproj:   # one kernel: its time is the x_proj stage's, the conv stage is empty
+        front = {"conv_silu_x_proj": stage_ms["conv_silu"] + stage_ms["x_proj"]}
+    else:
+        front = {"conv_silu": stage_ms["conv_silu"], "x_proj": stage_ms["x_proj"]}
     return {
-        "conv_silu": stage_ms["conv_silu"],
-        "x_proj": stage_ms["x_proj"],
+        **front,
         "norm_dt_proj": stage_ms["norm"] + stage_ms["dt_proj"],
         "scan_gate": stage_ms["scan_local"] + stage_ms["scan_carry"] + stage_ms["scan_full"],
     }
@@ -225,7 +231,7 @@ def time_prefill(jm, cfg, steps, warmup, hip, zoh=False):
     hip.destroy(evs)
     lay = jm.workspace_layout(dims)
     return {"ms": ms, "wall_s": wall, "stage_ms": stage_ms, "splits": lay.dbc_splits, "pieces": lay.scan_chunks,
-            "step_pct": percentiles(per_step)}
+            "step_pct": percentiles(per_step), "conv_in_xproj": lay.xproj_path == 4}
 
 
 def time_decode(jm, cfg, steps, warmup, hip, single=False):
@@ -618,7 +624,8 @@ def run_prefill(jm, cfg, args, hip):
     B, L, C, N, R = cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dt_rank
     tokens = B * L
     alg = algorithmic_bytes(B, L, C, N, R, 2)
-    groups = stage_groups(pre["stage_ms"])
+    groups = stage_groups(pre["stage_ms"], pre["conv_in_xproj"])
+    xp = "conv_silu_x_proj" if pre["conv_in_xproj"] else "x_proj"
     stages = {}
     for k, t in groups.items():
         gbs = alg[k] / (t * 1e-3) / 1e9 if t > 0 else 0.0
@@ -627,8 +634,8 @@ def run_prefill(jm, cfg, args, hip):
     for k, t in pre["stage_ms"].items():
         log(f"  {k:12s} {t * 1e3:9.2f} us")
     xflops = 2.0 * tokens * (R + 2 * N) * C
-    stages["x_proj"]["mfma_tflops"] = round(xflops / (groups["x_proj"] * 1e-3) / 1e12, 2)
-    stages["x_proj"]["frac_mfma_bf16"] = round(stages["x_proj"]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    stages[xp]["mfma_tflops"] = round(xflops / (groups[xp] * 1e-3) / 1e12, 2)
+    stages[xp]["frac_mfma_bf16"] = round(stages[xp]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
     dflops = 2.0 * tokens * R * C
     stages["norm_dt_proj"]["dt_proj_mfma_tflops"] = round(dflops / (pre["stage_ms"]["dt_proj"] * 1e-3) / 1e12, 2)
     # the dominant step: scan + gate (the local, carry and full passes of one launch of the scan), against

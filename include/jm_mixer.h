@@ -283,7 +283,9 @@ typedef struct jm_workspace_layout {
   int64_t total_bytes;
   int32_t xproj_path;     /* x_proj kernel layout: 0: bf16 matrix cores, 128-token x 288-column tiles;
                              1: bf16 matrix cores, 32-column groups (few tokens); 2: fp32 on the matrix cores;
-                             3: bf16 matrix cores, 256-token x 288-column tiles (32768 tokens or more) */
+                             3: bf16 matrix cores, 256-token x 288-column tiles (32768 tokens or more);
+                             4: as 3, with the conv1d + SiLU computed inside x_proj from x (one read of x,
+                                xc still written for the scan; the conv stage of the profiled call is empty) */
   int32_t reserved;
 } jm_workspace_layout;
 

@@ -437,6 +437,20 @@ void launch_conv_silu(bool bf16, const void* x, int64_t xs, const void* conv_w, 
   }
 }
 
+void launch_conv_head(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
+                      const void* conv_in, void* xc, int B, int L, int C, hipStream_t st) {
+  const int V = bf16 ? 8 : 4;
+  const int run = kTaps - 1;   // one run per sequence: its first 3 tokens
+  dim3 grid((C / V + 255) / 256, 1, B);
+  if (bf16)
+    hipLaunchKernelGGL(conv_silu_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, xs,
+                       (const bf16_t*)conv_w, (const bf16_t*)conv_b, (const bf16_t*)conv_in, (bf16_t*)xc, L, C,
+                       run);
+  else
+    hipLaunchKernelGGL(conv_silu_kernel<float>, grid, dim3(256), 0, st, (const float*)x, xs, (const float*)conv_w,
+                       (const float*)conv_b, (const float*)conv_in, (float*)xc, L, C, run);
+}
+
 void launch_conv_step(bool bf16, const void* x, int64_t xs, const void* conv_w, const void* conv_b,
                       const void* conv_in, void* xc, void* conv_out, int B, int C, hipStream_t st,
                       const int32_t* slots, int pool) {

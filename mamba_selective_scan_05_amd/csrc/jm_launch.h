@@ -24,6 +24,11 @@ void launch_conv_silu(bool bf16, const void* x, int64_t x_stride, const void* co
                       const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st,
                       const VarSeqs& v = VarSeqs{nullptr, nullptr, 0, 0});
 
+// The same conv + SiLU for the first min(L, 3) tokens of each of the B sequences only (the tokens whose left
+// context is the conv state).
+void launch_conv_head(bool bf16, const void* x, int64_t x_stride, const void* conv_w, const void* conv_b,
+                      const void* conv_state_in, void* xc, int B, int L, int C, hipStream_t st);
+
 // Packed batches, per sequence: conv_state_out = the last K-1 entries of the sequence's extended input
 // (x after its conv state), and for an empty sequence ssm_state_out = ssm_state_in (zeros for null).
 // Every read of a row precedes its write, so outputs may alias inputs; run it after the conv.
@@ -49,6 +54,13 @@ constexpr int kMaxXprojSplits = 16;
 // dbc partial sums: part[s, m, n] = sum over channel slice s of xc[m, k] * w[n, k].
 void launch_xproj(bool bf16, const void* xc, const void* w, float* part, int M, int N, int K, int splits,
                   bool narrow, hipStream_t st, bool tall = false);
+
+// bf16, the tall layout, B sequences of L tokens each (not packed): the conv + SiLU of launch_conv_silu
+// (xc [B*L, K] written, bit for bit the same) and launch_xproj's partial sums, in one kernel that reads x
+// once.  conv_xproj_fits(x_stride) must hold.
+bool conv_xproj_fits(int64_t x_stride);
+void launch_conv_xproj(const void* x, int64_t x_stride, const void* conv_w, const void* conv_b, const void* conv_in,
+                       void* xc, const void* w, float* part, int B, int L, int N, int K, int splits, hipStream_t st);
 
 // Sum the partials in slice order, RMSNorm the dt / B / C slices -> dln [M, R] (io dtype), bc [M, 2N].
 void launch_norm(bool bf16, const float* part, int splits, int M, int R, int N, const void* dt_norm_w,

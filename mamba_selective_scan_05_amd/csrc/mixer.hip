@@ -290,16 +290,22 @@ int run(const jm_mixer_dims* dims, const jm_mixer_weights* w, const void* x, con
     return e == hipSuccess && hipGetLastError() == hipSuccess ? JM_OK : JM_ERR_HIP;
   }
   marks.mark(0);
+  // long plain prefills: the conv runs inside x_proj (one read of x; the conv stage is then empty)
+  const bool conv_in_xproj = !step && !varlen && p.tall && jm::conv_xproj_fits(p.xs);
   if (step) {
     jm::launch_conv_step(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, conv_out, p.B, p.C, st, slots,
                          pool);
-  } else {
+  } else if (!conv_in_xproj) {
     jm::launch_conv_silu(p.bf16, x, p.xs, w->conv_w, w->conv_b, conv_in, xc, p.B, p.L, p.C, st, vs);
     // a packed batch's conv states (and the states of its empty sequences), once the conv has read them
     if (varlen) jm::launch_varlen_states(p.bf16, x, p.xs, conv_in, conv_out, h0, h_out, p.C, p.L, vs, st);
   }
   marks.mark(1);
-  jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st, p.tall);
+  if (conv_in_xproj)
+    jm::launch_conv_xproj(x, p.xs, w->conv_w, w->conv_b, conv_in, xc, w->x_proj_w, dbc, p.B, p.L, p.W, p.C,
+                          p.splits, st);
+  else
+    jm::launch_xproj(p.bf16, xc, w->x_proj_w, dbc, (int)p.T, p.W, p.C, p.splits, p.narrow, st, p.tall);
   marks.mark(2);
   jm::launch_norm(p.bf16, dbc, p.splits, (int)p.T, p.R, p.N, w->dt_norm_w, w->b_norm_w, w->c_norm_w,
                   dims->norm_eps, dln, bc, st);
@@ -529,7 +535,7 @@ int jm_mixer_prefill_workspace_layout(const jm_mixer_dims* dims, jm_workspace_la
   layout->dbc_splits = p.splits;
   layout->scan_chunks = p.P;
   layout->total_bytes = p.total;
-  layout->xproj_path = !p.bf16 ? 2 : p.narrow ? 1 : p.tall ? 3 : 0;
+  layout->xproj_path = !p.bf16 ? 2 : p.narrow ? 1 : p.tall ? (jm::conv_xproj_fits(p.xs) ? 4 : 3) : 0;
   layout->reserved = 0;
   return JM_OK;
 }

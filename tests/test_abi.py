@@ -103,6 +103,9 @@ def test_workspace_sizes_and_layout():
     assert lay.xproj_path == 0                                  # the 4K bf16 prefill: 288-column tiles
     assert jm.workspace_layout(jm.make_dims(256, 1, 8192, 256, jm.JM_BF16)).xproj_path == 1   # decode-sized
     assert jm.workspace_layout(jm.make_dims(1, 4096, 8192, 256, jm.JM_F32)).xproj_path == 2
+    # 32768 tokens or more: 256-token tiles with the conv inside x_proj (the 256K prefill, B = 8 x 4096)
+    assert jm.workspace_layout(jm.make_dims(1, 262144, 8192, 256, jm.JM_BF16)).xproj_path == 4
+    assert jm.workspace_layout(jm.make_dims(8, 4096, 8192, 256, jm.JM_BF16)).xproj_path == 4
     assert n >= T * C * 2 * 2 + lay.dbc_splits * T * W * 4 + T * 256 * 2 + T * 32 * 4
     offs = sorted([lay.xc, lay.dbc, lay.dln, lay.bc, lay.delta])
     assert offs[0] == 0 and all(o % 256 == 0 for o in offs) and offs[-1] < n

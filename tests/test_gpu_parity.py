@@ -117,12 +117,35 @@ def test_bf16_wide_xproj_tiles_across_sequences(with_state):
 
 @pytest.mark.parametrize("R", [16, 512])
 def test_bf16_tall_xproj_ragged(R):
-    # 32768 tokens or more: x_proj takes 256-token tiles (eight waves, two LDS stages); 40000 tokens leave a
-    # ragged last tile of 64, dt_rank 512 makes two 288-column groups
+    # 32768 tokens or more: x_proj takes 256-token tiles (eight waves, two LDS stages) and computes the conv
+    # itself; 40000 tokens leave a ragged last tile of 64, dt_rank 512 makes two 288-column groups (only the
+    # first writes xc)
     import mamba_selective_scan_05_amd as jm
     cfg = _small(f"tall_xproj_R{R}", 1, 40000, 256, R, "bf16", 23)
-    assert jm.workspace_layout(jm.make_dims(1, 40000, 256, R, jm.JM_BF16)).xproj_path == 3
+    assert jm.workspace_layout(jm.make_dims(1, 40000, 256, R, jm.JM_BF16)).xproj_path == 4
     _run_and_check(cfg)
+
+
+@pytest.mark.parametrize("with_state", [True, False])
+def test_bf16_conv_inside_tall_xproj_across_sequences(with_state):
+    # 3 x 11000 tokens: the conv runs inside the tall x_proj.  Sequence starts fall inside 256-token tiles
+    # (their first 3 tokens take the conv state as left context), x and z are strided views, the channels
+    # are split over two slices, the last tile is ragged.  Against the oracle, and xc bit for bit against the
+    # conv kernel on its own (the same tokens as one packed batch, whose conv runs as a separate pass).
+    import mamba_selective_scan_05_amd as jm
+    B, L, C = 3, 11000, 256
+    cfg = _small(f"conv_in_xproj_{'state' if with_state else 'nostate'}", B, L, C, 16, "bf16", 24)
+    lay = jm.workspace_layout(jm.make_dims(B, L, C, 16, jm.JM_BF16, x_row_stride=528, z_row_stride=528))
+    assert lay.xproj_path == 4 and lay.dbc_splits == 2
+    m, _, _, _ = _run_and_check(cfg, with_state=with_state, row_stride=528)
+    xc_fused = m._ws[lay.xc:lay.xc + B * L * C * 2].view(torch.bfloat16).clone()
+    a = make_activations(cfg, DEV, row_stride=528)
+    st = make_state(cfg, DEV) if with_state else {"conv_state": None, "ssm_state": None}
+    cu = torch.tensor([0, L, 2 * L, 3 * L], dtype=torch.int32, device=DEV)
+    m.prefill_varlen(a["x"].reshape(B * L, C), a["z"].reshape(B * L, C), cu, st["conv_state"], st["ssm_state"])
+    torch.cuda.synchronize()
+    xc_sep = m._ws[:B * L * C * 2].view(torch.bfloat16)
+    assert_bitwise("xc (conv inside x_proj vs the conv kernel)", xc_fused, xc_sep)
 
 
 @pytest.mark.parametrize("B,L", [(1, 450), (2, 155)])
