@@ -390,6 +390,12 @@ __global__ __launch_bounds__(kThreads2) void conv_xproj_tall_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     stage_barrier();
     auto dw = [](const uint4& v, int d) { return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w; };
+    auto set_dw = [](uint4& v, int d, uint32_t x) {
+      if (d == 0) v.x = x;
+      else if (d == 1) v.y = x;
+      else if (d == 2) v.z = x;
+      else v.w = x;
+    };
     // the SiLU outputs of channels c0 + 2d, c0 + 2d + 1 for one row, given its four inputs per channel
     auto conv2 = [&](int d, const float (&in)[2][4]) __attribute__((always_inline)) {
       const uint4 wv = *reinterpret_cast<const uint4*>(&P[(cj * 8 + 2 * d) * 2]);
@@ -407,21 +413,25 @@ __global__ __launch_bounds__(kThreads2) void conv_xproj_tall_kernel(
       }
       return f2bf2(o[0], o[1]);
     };
-    {
+    // the own rows as whole 16-byte chunks (8 lanes cover a row: no bank conflicts; per-dword accesses put
+    // the 64 lanes on 8 banks), converted in registers from the last row up: each output replaces an input
+    // that no row still to be converted reads
+    uint4 own[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {   // one dword (channel pair) of the 4 rows at a time
-        uint32_t win[7] = {dw(up[0], d), dw(up[1], d), dw(up[2], d)};
+    for (int i = 0; i < 4; ++i) own[i] = *reinterpret_cast<const uint4*>(&A32[widx(kHalo + 4 * cg + i)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) win[3 + i] = A32[widx(kHalo + 4 * cg + i) + d];
+    for (int d = 0; d < 4; ++d) {   // channels c0 + 2d, c0 + 2d + 1 (one dword of each row)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float in[2][4] = {{lo(win[i]), lo(win[i + 1]), lo(win[i + 2]), lo(win[i + 3])},
-                                  {hi(win[i]), hi(win[i + 1]), hi(win[i + 2]), hi(win[i + 3])}};
-          A32[widx(kHalo + 4 * cg + i) + d] = conv2(d, in);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // bounded register use
+      for (int i = 3; i >= 0; --i) {
+        auto src = [&](int j) { return j < 3 ? dw(up[j], d) : dw(own[j - 3], d); };   // input i - 3 + k
+        const float in[2][4] = {{lo(src(i)), lo(src(i + 1)), lo(src(i + 2)), lo(src(i + 3))},
+                                {hi(src(i)), hi(src(i + 1)), hi(src(i + 2)), hi(src(i + 3))}};
+        set_dw(own[i], d, conv2(d, in));
       }
+      __builtin_amdgcn_sched_barrier(0);   // one channel pair at a time: bounded register use
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&A32[widx(kHalo + 4 * cg + i)]) = own[i];
     if (edge) {
       // a row fewer than 3 positions into its sequence needs its conv state as left context: launch_conv_xproj
       // has already written those rows of xc (with the conv kernel itself); they replace what was computed
