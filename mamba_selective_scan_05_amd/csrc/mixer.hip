@@ -25,10 +25,14 @@ constexpr int64_t kAlign = 256;
 constexpr int kMaxSeqlen = 1 << 21;   // tokens of a prefill call (the conv's grid rows stay within 65536)
 constexpr int kMaxBatch = 1 << 16;    // sequences of a call (they index the grid's y / z axes, at most 65536)
 
-// Scan pieces: aim for this many 64-lane waves in the full pass (six per SIMD, the full pass's occupancy), with
-// pieces of at least kMinPiece tokens.  Measured against 4096, 2048 and 1024 waves: fewer pieces do less
-// local-pass work but leave the vector ALU idle (one wave per SIMD runs a token 2.3 times slower).
-constexpr int64_t kScanWaveTarget = 6144;
+// Scan pieces: aim for this many 64-lane waves in the full pass, with pieces of at least kMinPiece tokens.  That
+// is more than fit at once (five per SIMD at the full pass's register count, 5120): with more and shorter
+// pieces, the workgroups that finish early take more of them.  Measured at 256K tokens: 16384 waves (128
+// pieces) 14.7-14.8 ms against 15.3 ms with 6144 (the full pass 6.08-6.18 against 6.48-6.51 ms); 24576 no
+// better (the carry pass grows, 58 against 42 us); 5120 and 4096 (one round of five or four waves per SIMD)
+// 15.3 and 15.7 ms.  Pieces shorter than 128 tokens (the 4K prefill's 32 pieces) measured slower: 64 tokens
+// 337 us, 32 tokens 353 us, against 314-329 us.
+constexpr int64_t kScanWaveTarget = 16384;
 constexpr int kMinPiece = 128;
 // x_proj: split the contraction over channel slices until there are this many workgroups (one per CU).
 constexpr int kXprojWgTarget = 256;
