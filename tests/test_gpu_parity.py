@@ -148,6 +148,39 @@ def test_bf16_conv_inside_tall_xproj_across_sequences(with_state):
     assert_bitwise("xc (conv inside x_proj vs the conv kernel)", xc_fused, xc_sep)
 
 
+def test_bf16_conv_inside_tall_xproj_bias():
+    # the recipe's conv bias is zero: here a random one, through the conv inside x_proj (33000 tokens, two
+    # sequences, a ragged last tile) against the oracle and, bit for bit, against the packed-batch path (whose
+    # conv is the separate kernel); then no bias at all (a NULL pointer) equals a zero bias bit for bit
+    import mamba_selective_scan_05_amd as jm
+    B, L, C, R = 2, 16500, 256, 16
+    cfg = _small("conv_in_xproj_bias", B, L, C, R, "bf16", 25)
+    assert jm.workspace_layout(jm.make_dims(B, L, C, R, jm.JM_BF16)).xproj_path == 4
+    w = make_weights(cfg, DEV)
+    g = torch.Generator(device="cpu").manual_seed(26)
+    w["conv_b"] = (0.5 * torch.randn(C, generator=g)).to(cfg.torch_dtype).to(DEV)
+    m, out, _, _ = _run_and_check(cfg, w=w)
+    lay = jm.workspace_layout(m.dims(B, L))
+    xc_fused = m._ws[lay.xc:lay.xc + B * L * C * 2].view(torch.bfloat16).clone()
+    a = make_activations(cfg, DEV)
+    st = make_state(cfg, DEV)
+    cu = torch.tensor([0, L, 2 * L], dtype=torch.int32, device=DEV)
+    m.prefill_varlen(a["x"].reshape(B * L, C), a["z"].reshape(B * L, C), cu, st["conv_state"], st["ssm_state"])
+    torch.cuda.synchronize()
+    assert_bitwise("xc with a bias (conv inside x_proj vs the conv kernel)", xc_fused, m._ws[:B * L * C * 2].view(torch.bfloat16))
+    w0 = dict(w)
+    w0["conv_b"] = torch.zeros_like(w["conv_b"])
+    wn = {k: v for k, v in w.items() if k != "conv_b"}
+    outs = []
+    for ww in (w0, wn):
+        mm = _mixer(cfg, ww)
+        o, cs, hs = mm.prefill(a["x"], a["z"], st["conv_state"], st["ssm_state"])
+        torch.cuda.synchronize()
+        outs.append((o, cs, hs))
+    for i, name in enumerate(("out", "conv_state", "ssm_state")):
+        assert torch.equal(outs[0][i], outs[1][i]), f"{name}: NULL conv bias differs from a zero bias"
+
+
 @pytest.mark.parametrize("B,L", [(1, 450), (2, 155)])
 def test_bf16_few_token_tiles_dt_proj(B, L):
     # at most 8 64-token tiles: dt_proj takes 128-channel workgroups; at d_inner 8192 they hold two tiles
