@@ -29,11 +29,14 @@ namespace {
 
 constexpr int kN = 16;
 constexpr int kQ = 4;                  // states per lane
-// Tile sizes measured at B=1, L=4096, d_inner 8192 (bf16): sub-chunks of 4 tokens in pieces of 32 at four
-// waves per SIMD took 1073 us for the whole backward, against 1106 (8 / 64, two waves), 1174 (4 / 16) and
+// Tile sizes measured at B=1, L=4096, d_inner 8192 (bf16): sub-chunks of 4 tokens in pieces of 32 (registers for four
+// waves per SIMD) took 1073 us for the whole backward, against 1106 (8 / 64, two waves), 1174 (4 / 16) and
 // 1244 (8 / 32, three waves); keeping the decay factors and prefetching every input won over recomputing.
 constexpr int kSub = 4;                // tokens per recomputed sub-chunk
-constexpr int kBwdWavesPerSimd = 4;    // the second __launch_bounds__ argument
+// The second __launch_bounds__ argument: it caps the registers at 128.  The LDS (53 KB per workgroup) then
+// holds three workgroups per CU, i.e. three waves per SIMD, so the compiler reports its target of four unmet; a
+// target of three (130 registers) measured the same (backward 827-830 against 830-835 us).
+constexpr int kBwdWavesPerSimd = 4;
 constexpr int kPiece = kBwdPiece;      // tokens per piece (a multiple of kSub)
 constexpr int kNSub = kPiece / kSub;
 static_assert(kPiece % kSub == 0, "pieces hold whole sub-chunks");

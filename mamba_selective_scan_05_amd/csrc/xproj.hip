@@ -41,7 +41,6 @@ __device__ __forceinline__ bf16x8 lds_frag(const bf16_t* p) { return *reinterpre
 // in flight, with no staging registers.  LDS rows are 128 bytes (64 k) with no padding; 16-byte chunk j of
 // row r sits in slot j ^ (r & 7), which makes the fragment reads conflict-free (measured: 12 conflict cycles
 // per read without the swizzle, none with it).  A lane loads whichever global chunk belongs in its slot.
-constexpr int kStages = 3;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_void_t;
 __device__ __forceinline__ int swz(int r, int j) { return r * kKB + ((j ^ (r & 7)) << 3); }
@@ -274,10 +273,10 @@ __global__ __launch_bounds__(kThreads2) void xproj_mfma_tall_kernel(const bf16_t
 // 64-channel K block of the raw input x reaches LDS by the same direct loads as xc would, with 8 rows of left
 // context above the 256-token tile, and the block's conv weights and biases beside it.  The workgroup then
 // runs the conv in place: every thread keeps the 3 rows above its 4 rows x 8 channels in registers, all
-// threads meet at a barrier, and each converts its own rows one channel pair at a time, writes the SiLU
-// outputs over them, stores them to xc (the scan reads xc), and the block is multiplied as if xc had been
-// loaded.  x is read from HBM once and xc written once; the separate conv pass and x_proj's read of xc are
-// gone.  The arithmetic per element is conv_silu_kernel's (the same FMA order and SiLU, rounded once to
+// threads meet at a barrier, and each converts its own rows in registers and writes the SiLU outputs over
+// them; the block is then multiplied as if xc had been loaded, and its rows go to xc (the scan reads xc) one
+// block later, just before the stage is refilled.  x is read from HBM once and xc written once; the separate
+// conv pass and x_proj's read of xc are gone.  The arithmetic per element is conv_silu_kernel's (the same FMA order and SiLU, rounded once to
 // bf16), so xc matches it bit for bit.  The first 3 tokens of every sequence, whose left context is the conv
 // state, are computed beforehand by the conv kernel itself (launch_conv_xproj) and copied in from xc.
 constexpr int kHalo = 8;              // left-context rows staged above the tile (3 used; one whole load group)
@@ -329,8 +328,8 @@ __global__ __launch_bounds__(kThreads2) void conv_xproj_tall_kernel(
     const int row = (wave * kBL + q) * 8 + (lane >> 3);
     ob[q] = (uint32_t)(((int64_t)(min(n0 + row, N - 1) - n0) * K + (((lane & 7) ^ (row & 7)) << 3)) * 2);
   }
-  // conv parameters: lanes 0..31 bring two channels' taps each, lanes 32..39 eight biases each, the rest
-  // repeat lanes 0..23 (filler)
+  // conv parameters: lanes 0..31 bring two channels' taps each, lanes 32..39 eight biases each (without a
+  // bias, the taps of lanes 0..7 again), lanes 40..63 the taps of lanes 8..31 again (filler, never read)
   const bool has_bias = conv_b != nullptr;
   const char* pbase = lane >= 32 && lane < 40 && has_bias
                           ? reinterpret_cast<const char*>(conv_b) + (int64_t)(lane - 32) * 16
