@@ -108,7 +108,8 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false, bool si
   p.zs = d->z_row_stride ? d->z_row_stride : p.C;
 
   // x_proj split: channel slices of a multiple of 64, dividing C, until the grid is big enough.  When even
-  // the most slices leave the GPU short of workgroups, the narrow column layout multiplies the grid.
+  // the most slices leave the GPU short of workgroups, the narrow column layout multiplies the grid (not for
+  // long inputs: their 256-token tiles have no narrow form, and at 32768 tokens or more there are at least 128).
   p.splits = 1;
   p.narrow = false;
   p.tall = p.bf16 && p.T >= kXprojTallTokens;
@@ -122,7 +123,7 @@ Plan make_plan(const jm_mixer_dims* d, bool decode, bool varlen = false, bool si
         p.splits *= 2;
     };
     grow(jm::xproj_column_groups(p.W, false));
-    if (mtiles * jm::xproj_column_groups(p.W, false) * p.splits < kXprojWgTarget) {
+    if (!p.tall && mtiles * jm::xproj_column_groups(p.W, false) * p.splits < kXprojWgTarget) {
       p.narrow = true;
       grow(jm::xproj_column_groups(p.W, true));
     }

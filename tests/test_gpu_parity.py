@@ -148,6 +148,17 @@ def test_bf16_conv_inside_tall_xproj_across_sequences(with_state):
     assert_bitwise("xc (conv inside x_proj vs the conv kernel)", xc_fused, xc_sep)
 
 
+@pytest.mark.parametrize("L", [2, 4, 5])
+def test_bf16_conv_inside_tall_xproj_short_sequences(L):
+    # many short sequences reaching the long-input layout (at least 32768 tokens): with L = 2 every token is
+    # fewer than 3 positions into its sequence (all taken from the conv kernel's rows), with 4 and 5 most are
+    import mamba_selective_scan_05_amd as jm
+    B = -(-32768 // L)
+    cfg = _small(f"conv_in_xproj_L{L}", B, L, 64, 8, "bf16", 27)
+    assert jm.workspace_layout(jm.make_dims(B, L, 64, 8, jm.JM_BF16)).xproj_path == 4
+    _run_and_check(cfg)
+
+
 def test_bf16_conv_inside_tall_xproj_bias():
     # the recipe's conv bias is zero: here a random one, through the conv inside x_proj (33000 tokens, two
     # sequences, a ragged last tile) against the oracle and, bit for bit, against the packed-batch path (whose
