@@ -519,9 +519,9 @@ def time_serving(jm, steps, warmup):
 
 def time_training(jm, steps, warmup):
     """The gated scan alone at the 4K prefill's shape (B=1, L=4096, d_inner 8192, bf16): its forward
-    (jm_scan_forward) and backward (jm_scan_backward, recomputing the piece states), timed separately, and
-    the training pair that passes the states from one to the other (jm_scan_forward_train, then
-    jm_scan_backward given the saved states)."""
+    (jm_scan_forward) and backward (jm_scan_backward, recomputing the piece states), timed separately, the
+    saving forward (jm_scan_forward_train) and the backward given its saved states, alone and as the training
+    pair."""
     import torch
     from jm_inputs import CONFIGS, make_scan_problem
 
@@ -570,8 +570,9 @@ def time_training(jm, steps, warmup):
         bwd(i, saved)
 
     res = {"workload": f"{cfg.name}: the gated scan alone, B={B} L={L} d_inner={C}, bf16 I/O, fp32 state"}
+    bwd_saved = lambda i: bwd(i, saved)   # the states forward_train left in `saved` (timed after it)
     for name, step in (("forward", fwd), ("backward", bwd), ("forward_train", fwd_train),
-                       ("forward_train_plus_backward", train_pair)):
+                       ("backward_from_saved", bwd_saved), ("forward_train_plus_backward", train_pair)):
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -589,7 +590,10 @@ def time_training(jm, steps, warmup):
             res[name].update({"alg_ops": ops, "T_lane_ops_s": round(ach, 2),
                               "frac_alu": round(ach / VALU_PEAK_TOPS, 4)})
         log(f"  scan {name}: {ms * 1e3:.1f} us")
+    # the backward that recomputes the piece states, and the one a training step runs after
+    # jm_scan_forward_train, each against the plain forward
     res["backward_over_forward"] = round(res["backward"]["us"] / res["forward"]["us"], 2)
+    res["backward_from_saved_over_forward"] = round(res["backward_from_saved"]["us"] / res["forward"]["us"], 2)
     res["saved_states_bytes"] = saved.numel() * 4
     return res
 

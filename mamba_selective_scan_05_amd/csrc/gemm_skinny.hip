@@ -13,9 +13,11 @@
 // on timing.
 //
 // What bounds it is the rate at which L2 delivers X to the CUs (every workgroup re-reads X over its K slice:
-// for in_proj with 64-column blocks 512 MB of X against 134 MB of W).  With at least 128 blocks of 128
-// columns (in_proj at Jamba's widths) the workgroups take 128 columns over half the K range: half the X
-// re-reads, for 2 x M x N x 4 bytes of partial sums.
+// for in_proj with 64-column blocks 512 MB of X against 134 MB of W).  Whenever 128-column blocks still give a
+// workgroup per CU over whole K slices, the workgroups take 128 columns: half the X re-reads of 64-column
+// blocks, for splits x M x N x 4 bytes of partial sums.  256-column blocks (sixteen waves; two LDS stages of
+// 64 KB, since three do not fit) measured slower at Jamba's widths: in_proj 49-54 against 44.6 us, out_proj
+// 30 against 27.4 us, with twice the partial sums to add (one stage in flight does not hide the delivery).
 #include "jm_device.h"
 #include "jm_launch.h"
 
@@ -29,7 +31,6 @@ typedef __attribute__((address_space(1))) const void global_void_t;
 
 constexpr int kGM = 256;       // tokens per workgroup (the whole batch)
 constexpr int kGK = 64;        // K block staged in LDS
-constexpr int kGWideMin = 128; // 128-column blocks from this many of them on (two K slices: 256 workgroups)
 
 __device__ __forceinline__ int gswz(int r, int j) { return r * kGK + ((j ^ (r & 7)) << 3); }
 __device__ __forceinline__ bf16x8 gfrag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -198,36 +199,50 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
 
 }  // namespace
 
-// 128-column blocks when there are at least kGWideMin of them, else 64
-static int skinny_cols(int N) { return (N % 128 == 0 && N / 128 >= kGWideMin) ? 128 : 64; }
-
-int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes) {
-  if (M < 1 || M > kGM || N % 64 != 0 || K % kGK != 0) return 0;
-  // 128-column blocks over two K slices (half the X re-reads of 64-column blocks) when the slices and their
-  // partial sums fit; otherwise 64-column blocks, which then number at least 512 and need no split
-  if (skinny_cols(N) == 128 && (K / kGK) % 2 == 0 && K / kGK / 2 >= 4 && (int64_t)2 * M * N * 4 <= ws_bytes)
-    return 2;
-  const int gn = 64;
-  int splits = 1;
-  // split K until there are about as many workgroups as compute units, keeping every slice a whole number
-  // of K blocks and the partial sums within the workspace
-  while ((int64_t)(N / gn) * splits < 256 && (K / kGK) % (splits * 2) == 0 && K / kGK / (splits * 2) >= 4 &&
-         (int64_t)splits * 2 * M * N * 4 <= ws_bytes)
-    splits *= 2;
-  return splits;
+// Column-block width and K split for a shape.  Every workgroup re-reads X over its K slice, so the wider the
+// column block the fewer X bytes per W byte: 128-column blocks (eight waves) are taken whenever a split of K
+// into whole slices of at least 4 blocks gives the GPU a workgroup per CU and the partial sums fit (in_proj at
+// Jamba's widths: 128 blocks over 2 slices; out_proj: 32 blocks over 8 slices), otherwise 64-column blocks,
+// split the same way (shapes with at least 256 of them run unsplit).
+struct SkinnyPlan {
+  int gn, splits;
+};
+static SkinnyPlan skinny_plan(int M, int N, int K, int64_t ws_bytes) {
+  if (M < 1 || M > kGM || N % 64 != 0 || K % kGK != 0) return {0, 0};
+  const int kb = K / kGK;
+  auto splits_for = [&](int gn) {
+    int s = 1;
+    while ((int64_t)(N / gn) * s < 256 && kb % (s * 2) == 0 && kb / (s * 2) >= 4 &&
+           (int64_t)s * 2 * M * N * 4 <= ws_bytes)
+      s *= 2;
+    return s;
+  };
+  if (N % 128 == 0) {
+    const int s = splits_for(128);
+    if ((int64_t)(N / 128) * s >= 256) return {128, s};
+  }
+  return {64, splits_for(64)};
 }
+
+int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes) { return skinny_plan(M, N, K, ws_bytes).splits; }
 
 void launch_skinny_gemm(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* R, int64_t ldr, void* Y,
                         int64_t ldy, int M, int N, int K, int splits, float* part, hipStream_t st) {
-  const int gn = skinny_cols(N) == 128 && splits == 2 ? 128 : 64;   // as skinny_gemm_splits planned it
+  // as skinny_gemm_splits planned it (the workspace bound only limits the split, which the caller passes)
+  const int gn = skinny_plan(M, N, K, (int64_t)splits * M * N * 4).gn;
   dim3 grid((unsigned)((N / gn) * splits));
+  if (splits == 1) {
+    if (gn == 128)
+      hipLaunchKernelGGL((skinny_gemm_kernel<false, 128>), grid, dim3(512), 0, st, (const bf16_t*)X, ldx,
+                         (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, 1);
+    else
+      hipLaunchKernelGGL((skinny_gemm_kernel<false, 64>), grid, dim3(256), 0, st, (const bf16_t*)X, ldx,
+                         (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, 1);
+    return;
+  }
   if (gn == 128) {
     hipLaunchKernelGGL((skinny_gemm_kernel<true, 128>), grid, dim3(512), 0, st, (const bf16_t*)X, ldx,
                        (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, splits);
-  } else if (splits == 1) {
-    hipLaunchKernelGGL((skinny_gemm_kernel<false, 64>), grid, dim3(256), 0, st, (const bf16_t*)X, ldx,
-                       (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, 1);
-    return;
   } else {
     hipLaunchKernelGGL((skinny_gemm_kernel<true, 64>), grid, dim3(256), 0, st, (const bf16_t*)X, ldx,
                        (const bf16_t*)W, ldw, (const bf16_t*)R, ldr, (bf16_t*)Y, ldy, part, M, N, K, splits);

@@ -116,9 +116,10 @@ void launch_scan_carries(bool bf16, const ScanArgs& a, hipStream_t st);
 // The layer's projections for at most 256 tokens, bf16: Y[m, n] = sum_k X[m, k] W[n, k] (+ R[m, n]), row
 // strides ldx / ldw / ldr / ldy in elements (multiples of 8).  skinny_gemm_splits gives the K split for a
 // shape (0: the shape is not supported: M > 256, N or K not a multiple of 64), and with it the column-block
-// width launch_skinny_gemm uses (128 for two splits of a shape with at least 128 such blocks, else 64); with
-// more than one split the fp32 partial sums take splits * M * N * 4 bytes of `part`, within ws_bytes.  R may
-// alias Y.  Pass launch_skinny_gemm the splits skinny_gemm_splits returned for the same shape.
+// width launch_skinny_gemm uses (128 when a split into whole K slices gives at least 256 workgroups of 128
+// columns, else 64); with more than one split the fp32 partial sums take splits * M * N * 4 bytes of `part`,
+// within ws_bytes.  R may alias Y.  Pass launch_skinny_gemm the splits skinny_gemm_splits returned for the same
+// shape.
 int skinny_gemm_splits(int M, int N, int K, int64_t ws_bytes);
 void launch_skinny_gemm(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* R, int64_t ldr, void* Y,
                         int64_t ldy, int M, int N, int K, int splits, float* part, hipStream_t st);

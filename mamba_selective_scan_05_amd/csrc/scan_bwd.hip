@@ -200,7 +200,9 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
   const float* lb = a.bloc + (int64_t)b * P * (kN + 1) * C;
   float* gb = a.gin + (int64_t)b * P * kN * C;
   float U = a.dh_final ? a.dh_final[((int64_t)b * C + c) * kN + n] : 0.0f;
-  constexpr int kG = 8;
+  // pieces in groups of 16: all loads of a group are issued before its serial combine (one memory latency
+  // per group)
+  constexpr int kG = 16;
   for (int p0 = P - 1; p0 >= 0; p0 -= kG) {
     float ul[kG], sd[kG];
 #pragma unroll
@@ -466,16 +468,17 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __r
                                                                 float* __restrict__ dD, int C, int npieces) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;   // over C * N
   if (i >= C * kN) return;
-  // eight loads in flight per step (the partials are summed in piece order)
+  // sixteen loads in flight per step (the partials are summed in piece order; with 2 waves per SIMD the pass
+  // waits on one memory latency per step)
   auto sum = [&](const float* part, int64_t stride) __attribute__((always_inline)) {
     float s = 0.0f;
     int k = 0;
-    for (; k + 8 <= npieces; k += 8) {
-      float v[8];
+    for (; k + 16 <= npieces; k += 16) {
+      float v[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = part[(int64_t)(k + j) * stride + i];
+      for (int j = 0; j < 16; ++j) v[j] = part[(int64_t)(k + j) * stride + i];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += v[j];
+      for (int j = 0; j < 16; ++j) s += v[j];
     }
     for (; k < npieces; ++k) s += part[(int64_t)k * stride + i];
     return s;

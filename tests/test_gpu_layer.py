@@ -80,6 +80,13 @@ def test_layer_jamba_widths_512_tokens():
     _check_prefill(cfg, False)
 
 
+def test_layer_jamba_widths_200_tokens():
+    # at most 256 tokens at Jamba's widths: both projections on the weight-streaming kernel with the column
+    # blocks and K splits of the benched B = 256 decode step, here with a ragged last token group
+    cfg = LAYER_CONFIGS[0].replace(name="jamba_layer_L200", seqlen=200)
+    _check_prefill(cfg, False)
+
+
 @pytest.mark.parametrize("B,L", [(2, 100), (1, 1), (1, 256)])
 def test_layer_prefill_up_to_256_tokens_in_place(B, L):
     # at most 256 tokens in bf16: both projections run on the library's weight-streaming kernel; d_inner 1024
@@ -141,3 +148,27 @@ def test_layer_rejects_bad_dims():
     s = jm.call_layer(d, layer.packed, x.data_ptr(), x.data_ptr(), None, co.data_ptr(), None, ho.data_ptr(),
                       ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
     assert s == jm._lib.JM_ERR_WORKSPACE
+
+
+def test_layer_decode_unsplit_wide_blocks():
+    # d_inner 16384 makes in_proj 32768 columns wide over K = d_model = 64: 256 blocks of 128 columns fill the
+    # GPU without a K split, so the weight-streaming kernel writes bf16 results directly (no partial sums)
+    cfg = MixerConfig("layer_skinny_unsplit", batch=3, seqlen=1, d_inner=16384, dt_rank=16, io_dtype="bf16",
+                      seed=37, d_model=64, with_state=True)
+    w = make_weights(cfg, DEV)
+    lw = make_layer_weights(cfg, DEV)
+    st = make_state(cfg, DEV)
+    xs = make_layer_input(cfg, DEV, steps=2)
+    layer = _layer(cfg, w, lw)
+    cs, hs = st["conv_state"].clone(), st["ssm_state"].clone()
+    c64, h64 = to_f64(st["conv_state"]), to_f64(st["ssm_state"])
+    w64, lw64 = weights_f64(w), weights_f64(lw)
+    for t in range(xs.shape[1]):
+        x = xs[:, t].contiguous()
+        out, _, _ = layer.decode_step(x, cs, hs, in_place=True)
+        torch.cuda.synchronize()
+        ro, c64, h64 = oracle.layer_decode_step(to_f64(x), lw64, w64, cfg.dt_rank, cfg.d_state, c64, h64,
+                                                cfg.norm_eps, 1e-6)
+        assert_close(f"out[{t}]", out, ro, "bf16")
+    assert_close("h_final", hs, h64, "bf16")
+    assert_close("conv_state", cs, c64, "bf16")
