@@ -447,15 +447,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
                                                             int64_t rows, int nblk) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over rows * 2N
   if (i >= rows * 2 * kN) return;
-  // eight loads in flight per step (the partials are summed in block order)
+  // sixteen loads in flight per step (the partials are summed in block order)
   float s = 0.0f;
   int k = 0;
-  for (; k + 8 <= nblk; k += 8) {
-    float v[8];
+  for (; k + 16 <= nblk; k += 16) {
+    float v[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = pbc[(int64_t)(k + j) * rows * 2 * kN + i];
+    for (int j = 0; j < 16; ++j) v[j] = pbc[(int64_t)(k + j) * rows * 2 * kN + i];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s += v[j];
+    for (int j = 0; j < 16; ++j) s += v[j];
   }
   for (; k < nblk; ++k) s += pbc[(int64_t)k * rows * 2 * kN + i];
   dbc[i] = s;
