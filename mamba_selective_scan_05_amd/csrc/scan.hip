@@ -384,8 +384,8 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
   }
   // pieces in groups (16 for plain batches; 8 for packed batches, which also look up each piece's sequence):
   // all loads of a group are issued before its serial combine, so a group costs one memory latency.  With
-  // 128 pieces (256K tokens) groups of 16 against 8 took the pass from 41 to ~31 us; with 16 pieces (B = 8)
-  // groups of 32 made it slower (30 -> 37 us: the clamped surplus loads and the registers).
+  // 128 pieces (256K tokens) groups of 16 against 8 took the pass from 38.5 to 29.4 us (rocprofv3); groups of
+  // 32 made the 16-piece B = 8 case slower (30 -> 37 us: the clamped surplus loads and the registers).
   constexpr int kG = VAR ? 8 : 16;
   for (int p0 = VAR ? 0 : 1; p0 < P; p0 += kG) {
     float hl[kG], sd[kG], hi[kG];
