@@ -20,31 +20,38 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 
-// norm: WPT waves per token (1, or 4 when there are few tokens), each summing S / WPT of the x_proj slices.
-// S (the number of slices) and COLS (columns per lane, 64 columns apart) are compile-time so that every
-// partial-sum load is unconditional (columns past W re-read column W - 1 and are dropped): all of a lane's
-// loads are in flight together, then added in slice order; with WPT = 4 the four waves' sums are added in
-// wave order through LDS (a fixed order: the result does not depend on timing).
-template <typename T, int S, int COLS, int WPT>
+// norm: WPT waves per token (1, or 4 when there are few tokens), each summing S / WPT of the x_proj slices;
+// with a single slice (long inputs) a wave takes TPW = 4 consecutive tokens, since a wave per token moves only a
+// few hundred bytes (256K tokens: 136 -> 113 us; two tokens per wave with two slices, B = 8 x 4K, measured
+// 1 us slower, so they keep a wave per token).  S (the number of slices) and COLS (columns per lane, 64 columns apart) are
+// compile-time so that every partial-sum load is unconditional (columns past W re-read column W - 1 and tokens
+// past M re-read token M - 1; both are dropped): all of a lane's loads are in flight together, then added in
+// slice order; with WPT = 4 the four waves' sums are added in wave order through LDS (a fixed order: the
+// result does not depend on timing).
+template <typename T, int S, int COLS, int WPT, int TPW = 1>
 __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ part, int M, int R, int N,
                                                    const T* __restrict__ wdt, const T* __restrict__ wb,
                                                    const T* __restrict__ wc, float eps, T* __restrict__ dln,
                                                    float* __restrict__ bc) {
   static_assert(WPT == 1 || WPT == 4, "one wave per token or a whole workgroup per token");
+  static_assert(WPT == 1 || TPW == 1, "several tokens per wave only with one wave per token");
   constexpr int SW = S / WPT;                          // slices per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = WPT == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
-  if (WPT == 1 && m >= M) return;
+  const int m0 = WPT == 1 ? (blockIdx.x * 4 + wave) * TPW : blockIdx.x;
+  if (WPT == 1 && m0 >= M) return;
   const int sub = WPT == 1 ? 0 : wave;
   const int W = R + 2 * N;
   const int64_t slice = (int64_t)M * W;
-  const float* src = part + (int64_t)m * W + (int64_t)sub * SW * slice;
-  float pv[COLS][SW], wn[COLS];
+  float pv[TPW][COLS][SW], wn[COLS];
 #pragma unroll
-  for (int i = 0; i < COLS; ++i) {
-    const int col = min(lane + 64 * i, W - 1);
+  for (int t = 0; t < TPW; ++t) {
+    const float* src = part + (int64_t)min(m0 + t, M - 1) * W + (int64_t)sub * SW * slice;
 #pragma unroll
-    for (int p = 0; p < SW; ++p) pv[i][p] = src[p * slice + col];
+    for (int i = 0; i < COLS; ++i) {
+      const int col = min(lane + 64 * i, W - 1);
+#pragma unroll
+      for (int p = 0; p < SW; ++p) pv[t][i][p] = src[p * slice + col];
+    }
   }
   // the norm weight of each column, loaded with the partial sums (clamped indices, no branches) so that it
   // is not a second round trip to memory after the reduction
@@ -56,48 +63,53 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ par
     const float c = io<T>::ld(wc + min(max(col - R - N, 0), N - 1));
     wn[i] = col < R ? a : col < R + N ? b : c;
   }
-  float v[COLS];
 #pragma unroll
-  for (int i = 0; i < COLS; ++i) {
-    float s = 0.f;
+  for (int t = 0; t < TPW; ++t) {
+    const int m = m0 + t;
+    if (TPW > 1 && m >= M) break;
+    float v[COLS];
 #pragma unroll
-    for (int p = 0; p < SW; ++p) s += pv[i][p];
-    v[i] = s;
-  }
-  if (WPT > 1) {
-    __shared__ float red[4][COLS * 64];
+    for (int i = 0; i < COLS; ++i) {
+      float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < COLS; ++i) red[wave][i * 64 + lane] = v[i];
-    __syncthreads();
-    if (wave != 0) return;
+      for (int p = 0; p < SW; ++p) s += pv[t][i][p];
+      v[i] = s;
+    }
+    if (WPT > 1) {
+      __shared__ float red[4][COLS * 64];
 #pragma unroll
-    for (int i = 0; i < COLS; ++i)
-      v[i] = ((red[0][i * 64 + lane] + red[1][i * 64 + lane]) + red[2][i * 64 + lane]) + red[3][i * 64 + lane];
-  }
-  float ss_dt = 0.f, ss_b = 0.f, ss_c = 0.f;
+      for (int i = 0; i < COLS; ++i) red[wave][i * 64 + lane] = v[i];
+      __syncthreads();
+      if (wave != 0) return;
 #pragma unroll
-  for (int i = 0; i < COLS; ++i) {
-    const int col = lane + 64 * i;
-    const float sq = v[i] * v[i];
-    if (col < R) ss_dt += sq;
-    else if (col < R + N) ss_b += sq;
-    else if (col < W) ss_c += sq;
-  }
-  ss_dt = wave_sum(ss_dt);
-  ss_b = wave_sum(ss_b);
-  ss_c = wave_sum(ss_c);
-  const float r_dt = 1.0f / sqrtf(ss_dt / R + eps);
-  const float r_b = 1.0f / sqrtf(ss_b / N + eps);
-  const float r_c = 1.0f / sqrtf(ss_c / N + eps);
+      for (int i = 0; i < COLS; ++i)
+        v[i] = ((red[0][i * 64 + lane] + red[1][i * 64 + lane]) + red[2][i * 64 + lane]) + red[3][i * 64 + lane];
+    }
+    float ss_dt = 0.f, ss_b = 0.f, ss_c = 0.f;
 #pragma unroll
-  for (int i = 0; i < COLS; ++i) {
-    const int col = lane + 64 * i;
-    if (col < R) {
-      io<T>::st(dln + (int64_t)m * R + col, v[i] * r_dt * wn[i]);
-    } else if (col < R + N) {
-      bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_b * wn[i];
-    } else if (col < W) {
-      bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_c * wn[i];
+    for (int i = 0; i < COLS; ++i) {
+      const int col = lane + 64 * i;
+      const float sq = v[i] * v[i];
+      if (col < R) ss_dt += sq;
+      else if (col < R + N) ss_b += sq;
+      else if (col < W) ss_c += sq;
+    }
+    ss_dt = wave_sum(ss_dt);
+    ss_b = wave_sum(ss_b);
+    ss_c = wave_sum(ss_c);
+    const float r_dt = 1.0f / sqrtf(ss_dt / R + eps);
+    const float r_b = 1.0f / sqrtf(ss_b / N + eps);
+    const float r_c = 1.0f / sqrtf(ss_c / N + eps);
+#pragma unroll
+    for (int i = 0; i < COLS; ++i) {
+      const int col = lane + 64 * i;
+      if (col < R) {
+        io<T>::st(dln + (int64_t)m * R + col, v[i] * r_dt * wn[i]);
+      } else if (col < R + N) {
+        bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_b * wn[i];
+      } else if (col < W) {
+        bc[(int64_t)m * 2 * N + (col - R)] = v[i] * r_c * wn[i];
+      }
     }
   }
 }
@@ -107,10 +119,14 @@ void launch_norm_cols(int splits, dim3 grid, hipStream_t st, const float* part, 
                       const T* wb, const T* wc, float eps, T* dln, float* bc) {
   switch (splits) {
 #define JM_NORM_CASE(S)                                                                                       \
-  case S:                                                                                                     \
-    hipLaunchKernelGGL((norm_kernel<T, S, COLS, (S >= WPT ? WPT : 1)>), grid, dim3(256), 0, st, part, M, R, N, \
-                       wdt, wb, wc, eps, dln, bc);                                                            \
-    break;
+  case S: {                                                                                                   \
+    constexpr int wpt = S >= WPT ? WPT : 1;                                                                   \
+    constexpr int tpw = wpt == 1 && S == 1 ? 4 : 1;                                                           \
+    const dim3 g = wpt == 1 ? dim3((unsigned)((M + 4 * tpw - 1) / (4 * tpw))) : grid;                         \
+    hipLaunchKernelGGL((norm_kernel<T, S, COLS, wpt, tpw>), g, dim3(256), 0, st, part, M, R, N, wdt, wb, wc,  \
+                       eps, dln, bc);                                                                         \
+    break;                                                                                                    \
+  }
     JM_NORM_CASE(1)
     JM_NORM_CASE(2)
     JM_NORM_CASE(4)
